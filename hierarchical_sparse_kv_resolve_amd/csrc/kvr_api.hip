@@ -1,0 +1,434 @@
+// C ABI of the gfx950 sparse KV row resolver: argument checking, context
+// state and launch sequencing.  Every entry point returns a kvr_status and
+// records a message for kvr_last_error(); no exception crosses the ABI.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kvr_internal.h"
+
+namespace kvr {
+bool tile_magic_exact(int32_t row_bytes);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(KVR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return KVR_OK;
+}
+
+int check_ctx(const kvr_ctx *c, bool need_meta = true)
+{
+    if (!c)
+        return fail(KVR_E_ARG, "null context");
+    if (need_meta && !c->meta_bound)
+        return fail(KVR_E_ARG, "metadata not bound");
+    return KVR_OK;
+}
+
+int check_layer(const kvr_ctx *c, int32_t layer)
+{
+    if (layer < 0 || layer >= c->cfg.n_layers)
+        return fail(KVR_E_ARG, "layer %d outside [0, %d)", layer, c->cfg.n_layers);
+    if (!c->layer_bound[layer])
+        return fail(KVR_E_ARG, "layer %d not bound", layer);
+    return KVR_OK;
+}
+
+int check_n(const kvr_ctx *c, int32_t n)
+{
+    if (n < 0 || n > c->cfg.n_req)
+        return fail(KVR_E_ARG, "request count %d outside [0, %d]", n, c->cfg.n_req);
+    return KVR_OK;
+}
+
+// The stream must belong to the context's device.
+int check_stream(const kvr_ctx *c, hipStream_t s)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != c->device)
+        return fail(KVR_E_ARG, "current device %d is not the context's device %d", dev, c->device);
+    (void)s;
+    return KVR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvr_last_error(void) { return g_err; }
+
+int kvr_create(const kvr_config *cfg, kvr_ctx **out)
+{
+    if (!out)
+        return fail(KVR_E_ARG, "null output pointer");
+    *out = nullptr;
+    if (!cfg)
+        return fail(KVR_E_ARG, "null config");
+    const kvr_config &c = *cfg;
+    if (c.n_req < 1 || c.n_layers < 1)
+        return fail(KVR_E_ARG, "n_req and n_layers must be >= 1");
+    if (c.history_rows < 0 || c.max_new_rows < 0 ||
+        (int64_t)c.history_rows + c.max_new_rows >= (int64_t)INT32_MAX)
+        return fail(KVR_E_ARG, "history_rows + max_new_rows must be in [0, 2^31 - 1)");
+    if (c.page_rows < 1)
+        return fail(KVR_E_ARG, "page_rows must be >= 1");
+    if (c.tail_rows < 0 || c.tail_rows >= (1 << 30))
+        return fail(KVR_E_ARG, "tail_rows must be in [0, 2^30)");
+    if (c.hot_slots < 1 || c.hot_slots > kvr::kMaxHotSlots)
+        return fail(KVR_E_ARG, "hot_slots must be in [1, %d]", kvr::kMaxHotSlots);
+    if (c.row_bytes < 16 || c.row_bytes % 16 != 0)
+        return fail(KVR_E_ARG, "row_bytes must be a positive multiple of 16");
+    if (c.sel_cap < 1 || c.sel_cap > kvr::kMaxSelCap)
+        return fail(KVR_E_ARG, "sel_cap must be in [1, %d]", kvr::kMaxSelCap);
+    if (c.reserved != 0)
+        return fail(KVR_E_ARG, "reserved must be 0");
+    if (c.pool_pages < 0 || c.pool_pages * (int64_t)c.page_rows >= ((int64_t)1 << 30))
+        return fail(KVR_E_ARG, "pool_pages * page_rows must be in [0, 2^30)");
+    if (!kvr::tile_magic_exact(c.row_bytes))
+        return fail(KVR_E_ARG, "row_bytes %d too large for the copy tiles", c.row_bytes);
+
+    kvr_ctx *ctx = new (std::nothrow) kvr_ctx();
+    if (!ctx)
+        return fail(KVR_E_ARG, "out of host memory");
+    ctx->cfg = c;
+    kvr::Shape &sh = ctx->shape;
+    sh.n_req = c.n_req;
+    sh.n_layers = c.n_layers;
+    sh.H = c.history_rows;
+    sh.max_new = c.max_new_rows;
+    sh.P = c.page_rows;
+    sh.T = c.tail_rows;
+    sh.B = c.hot_slots;
+    sh.R = c.row_bytes;
+    sh.sel_cap = c.sel_cap;
+    sh.n_pages = (c.history_rows + c.page_rows - 1) / c.page_rows;
+    sh.full_rows = (c.history_rows / c.page_rows) * c.page_rows;
+    sh.pool_rows = c.pool_pages * c.page_rows;
+    sh.host_rows = (int64_t)c.history_rows + c.max_new_rows;
+    ctx->resolve_lds = kvr::resolve_lds_bytes(sh);
+
+    hipError_t e = hipGetDevice(&ctx->device);
+    if (e != hipSuccess) {
+        delete ctx;
+        return hip_fail(e, "hipGetDevice");
+    }
+    ctx->layers_h = new (std::nothrow) kvr::LayerPtrs[c.n_layers]();
+    ctx->layer_bound = new (std::nothrow) bool[c.n_layers]();
+    if (!ctx->layers_h || !ctx->layer_bound) {
+        kvr_destroy(ctx);
+        return fail(KVR_E_ARG, "out of host memory");
+    }
+    e = hipMalloc(&ctx->layers_d, sizeof(kvr::LayerPtrs) * c.n_layers);
+    if (e != hipSuccess) {
+        ctx->layers_d = nullptr;
+        kvr_destroy(ctx);
+        return hip_fail(e, "hipMalloc(layer table)");
+    }
+    e = hipMemset(ctx->layers_d, 0, sizeof(kvr::LayerPtrs) * c.n_layers);
+    if (e == hipSuccess)
+        e = kvr::prepare_resolve_kernel();
+    if (e == hipSuccess)
+        e = kvr::prepare_dedup_kernel();
+    if (e != hipSuccess) {
+        kvr_destroy(ctx);
+        return hip_fail(e, "kernel set-up");
+    }
+    *out = ctx;
+    return ok();
+}
+
+int kvr_destroy(kvr_ctx *ctx)
+{
+    if (!ctx)
+        return ok();
+    if (ctx->layers_d)
+        (void)hipFree(ctx->layers_d);
+    delete[] ctx->layers_h;
+    delete[] ctx->layer_bound;
+    delete ctx;
+    return ok();
+}
+
+int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, const int32_t *page_map, const uint8_t *host_valid,
+                      int32_t *tag, uint32_t *stamp, uint32_t *clock)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (!L || !tag || !stamp || !clock)
+        return fail(KVR_E_ARG, "L, tag, stamp and clock are required");
+    if (ctx->shape.n_pages > 0 && (!page_map || !host_valid))
+        return fail(KVR_E_ARG, "page_map and host_valid are required when H > 0");
+    ctx->L = L;
+    ctx->page_map = page_map;
+    ctx->host_valid = host_valid;
+    ctx->tag = tag;
+    ctx->stamp = stamp;
+    ctx->clock = clock;
+    ctx->meta_bound = true;
+    return ok();
+}
+
+int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, const void *pool, void *hot, void *host)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (layer < 0 || layer >= ctx->cfg.n_layers)
+        return fail(KVR_E_ARG, "layer %d outside [0, %d)", layer, ctx->cfg.n_layers);
+    if (!hot || !host)
+        return fail(KVR_E_ARG, "hot and host are required");
+    if (ctx->shape.T > 0 && !tail)
+        return fail(KVR_E_ARG, "tail is required when T > 0");
+    if (ctx->shape.pool_rows > 0 && !pool)
+        return fail(KVR_E_ARG, "pool is required when pool_pages > 0");
+    void *host_dev = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&host_dev, host, 0);
+    if (e != hipSuccess || !host_dev)
+        return fail(KVR_E_ARG, "host store is not device-mapped pinned memory (%s)",
+                    hipGetErrorString(e));
+    kvr::LayerPtrs lp;
+    lp.tail = static_cast<uint8_t *>(tail);
+    lp.pool = static_cast<const uint8_t *>(pool);
+    lp.hot = static_cast<uint8_t *>(hot);
+    lp.host = static_cast<uint8_t *>(host_dev);
+    e = hipMemcpy(ctx->layers_d + layer, &lp, sizeof lp, hipMemcpyHostToDevice);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpy(layer table)");
+    ctx->layers_h[layer] = lp;
+    ctx->layer_bound[layer] = true;
+    return ok();
+}
+
+int kvr_init_state(kvr_ctx *ctx, void *stream)
+{
+    if (int rc = check_ctx(ctx))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    hipError_t e = kvr::launch_init_state(ctx, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "init_state launch");
+}
+
+int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                    int32_t *status, void *stream)
+{
+    if (int rc = check_ctx(ctx))
+        return rc;
+    if (int rc = check_n(ctx, n))
+        return rc;
+    for (int32_t l = 0; l < ctx->cfg.n_layers; ++l)
+        if (int rc = check_layer(ctx, l))
+            return rc;
+    if (n > 0 && !new_rows)
+        return fail(KVR_E_ARG, "new_rows is required");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    hipError_t e = kvr::launch_append(ctx, n, req_ids, static_cast<const uint8_t *>(new_rows),
+                                      status, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "append launch");
+}
+
+int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *sel,
+                     const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
+                     int32_t *fill_count, int32_t fill_layer, int32_t *status, kvr_stats *stats,
+                     void *stream)
+{
+    if (int rc = check_ctx(ctx))
+        return rc;
+    if (int rc = check_n(ctx, n))
+        return rc;
+    if (stride < 0 || stride > ctx->cfg.sel_cap)
+        return fail(KVR_E_ARG, "stride %d outside [0, sel_cap=%d]", stride, ctx->cfg.sel_cap);
+    if (n > 0 && ((stride > 0 && (!sel || !loc)) || !fills || !fill_count || !status))
+        return fail(KVR_E_ARG, "sel, loc, fills, fill_count and status are required");
+    if (fill_layer != -1)
+        if (int rc = check_layer(ctx, fill_layer))
+            return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    hipError_t e = kvr::launch_resolve(ctx, n, req_ids, sel, sel_count, stride, loc, fills,
+                                       fill_count, status, stats, fill_layer >= 0 ? 1 : 0, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "resolve launch");
+    if (fill_layer >= 0) {
+        e = kvr::launch_refill(ctx, fill_layer, n, req_ids, fills, fill_count, nullptr, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "refill launch");
+    }
+    return ok();
+}
+
+int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                    const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
+                    int32_t stride, void *const *out, int32_t *status, void *stream)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (int rc = check_n(ctx, n))
+        return rc;
+    if (n_layers < 0 || (n_layers > 0 && (!layers || !out)))
+        return fail(KVR_E_ARG, "layers and out are required");
+    if (stride < 0)
+        return fail(KVR_E_ARG, "negative stride");
+    if (n > 0 && stride > 0 && n_layers > 0 && !loc)
+        return fail(KVR_E_ARG, "loc is required");
+    kvr::GatherTarget *targets = nullptr;
+    if (n_layers > 0) {
+        targets = static_cast<kvr::GatherTarget *>(std::malloc(sizeof(kvr::GatherTarget) * n_layers));
+        if (!targets)
+            return fail(KVR_E_ARG, "out of host memory");
+    }
+    for (int32_t t = 0; t < n_layers; ++t) {
+        if (int rc = check_layer(ctx, layers[t])) {
+            std::free(targets);
+            return rc;
+        }
+        if (!out[t] && n > 0 && stride > 0) {
+            std::free(targets);
+            return fail(KVR_E_ARG, "out[%d] is null", t);
+        }
+        targets[t].layer = layers[t];
+        targets[t].out = static_cast<uint8_t *>(out[t]);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_stream(ctx, s);
+    if (rc == KVR_OK && n > 0 && stride > 0 && n_layers > 0) {
+        hipError_t e = kvr::launch_gather(ctx, targets, n_layers, n, req_ids, loc, count, stride,
+                                          status, s);
+        rc = e == hipSuccess ? KVR_OK : hip_fail(e, "gather launch");
+    }
+    std::free(targets);
+    return rc == KVR_OK ? ok() : rc;
+}
+
+int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,
+                                int32_t *union_rows, int32_t *union_count, int32_t *map,
+                                void *stream)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (int rc = check_n(ctx, n))
+        return rc;
+    if (q < 1 || k < 0 || (int64_t)q * k > kvr::kMaxUnion)
+        return fail(KVR_E_ARG, "need q >= 1, k >= 0 and q * k <= %d", kvr::kMaxUnion);
+    if (n > 0 && (!union_count || (q * k > 0 && (!sel || !union_rows || !map))))
+        return fail(KVR_E_ARG, "sel, union_rows, union_count and map are required");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    hipError_t e = kvr::launch_dedup(n, q, k, sel, union_rows, union_count, map, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "dedup launch");
+}
+
+int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n,
+                        const int32_t *req_ids, const uint32_t *src_loc, uint32_t *dst_loc,
+                        const int32_t *count, int32_t stride, const kvr_fill *fills,
+                        const int32_t *fill_count, int32_t *status, void *stream)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (int rc = check_n(ctx, n))
+        return rc;
+    if (mode != KVR_REUSE_SHARED_SOURCE && mode != KVR_REUSE_DISTINCT_PAYLOAD)
+        return fail(KVR_E_ARG, "unknown reuse mode %d", mode);
+    if (stride < 0)
+        return fail(KVR_E_ARG, "negative stride");
+    if (dst_loc && !src_loc && stride > 0 && n > 0)
+        return fail(KVR_E_ARG, "src_loc is required to copy locations");
+    if (mode == KVR_REUSE_DISTINCT_PAYLOAD) {
+        if (int rc = check_layer(ctx, dst_layer))
+            return rc;
+        if (n > 0 && (!fills || !fill_count))
+            return fail(KVR_E_ARG, "fills and fill_count are required to replay fills");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    if (mode == KVR_REUSE_DISTINCT_PAYLOAD) {
+        hipError_t e = kvr::launch_refill(ctx, dst_layer, n, req_ids, fills, fill_count, status, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "replay launch");
+    }
+    if (dst_loc && stride > 0 && dst_loc != src_loc) {
+        hipError_t e = kvr::launch_copy_loc(ctx, n, src_loc, dst_loc, count, stride, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "location copy launch");
+    }
+    return ok();
+}
+
+int kvr_status_summary(const int32_t *status, int32_t n, int32_t *first_bad)
+{
+    if ((!status && n > 0) || n < 0)
+        return fail(KVR_E_ARG, "bad status array");
+    int bad = 0;
+    int first = -1;
+    for (int32_t i = 0; i < n; ++i) {
+        if (status[i] != KVR_OK) {
+            if (first < 0)
+                first = i;
+            ++bad;
+        }
+    }
+    if (first_bad)
+        *first_bad = first;
+    g_err[0] = '\0';
+    return bad;
+}
+
+int kvr_host_alloc(size_t bytes, void **out)
+{
+    if (!out)
+        return fail(KVR_E_ARG, "null output pointer");
+    *out = nullptr;
+    hipError_t e = hipHostMalloc(out, bytes ? bytes : 1, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return hip_fail(e, "hipHostMalloc");
+    }
+    return ok();
+}
+
+int kvr_host_free(void *ptr)
+{
+    if (!ptr)
+        return ok();
+    hipError_t e = hipHostFree(ptr);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipHostFree");
+}
+
+}  // extern "C"

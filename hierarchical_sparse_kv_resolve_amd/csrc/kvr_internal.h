@@ -1,0 +1,91 @@
+// Internal declarations of the gfx950 sparse KV row resolver library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvr.h"
+
+namespace kvr {
+
+constexpr int kMaxHotSlots = 8192;
+constexpr int kMaxSelCap = 8192;
+constexpr int kMaxUnion = 16384;       // q * k of one verification block
+constexpr int kGatherLayersPerLaunch = 24;
+
+// Location word layout (bits 31..30 place, 29..0 index).
+constexpr uint32_t kPlaceShift = 30;
+constexpr uint32_t kIndexMask = 0x3FFFFFFFu;
+
+// Device-side pointers of one payload layer.
+struct LayerPtrs {
+    uint8_t *tail;        // [n_req][T][R]
+    const uint8_t *pool;  // [pool_pages][P][R]
+    uint8_t *hot;         // [n_req][B][R]
+    uint8_t *host;        // [n_req][H + max_new][R], device alias of pinned memory
+};
+
+// Shape constants every kernel needs.
+struct Shape {
+    int32_t n_req, n_layers, H, max_new, P, T, B, R;
+    int32_t sel_cap, n_pages, full_rows;  // full_rows = (H / P) * P
+    int64_t pool_rows;                    // pool_pages * P
+    int64_t host_rows;                    // H + max_new
+};
+
+}  // namespace kvr
+
+struct kvr_ctx {
+    kvr_config cfg;
+    kvr::Shape shape;
+    int device;
+    // metadata (device)
+    int32_t *L;
+    const int32_t *page_map;
+    const uint8_t *host_valid;
+    int32_t *tag;
+    uint32_t *stamp;
+    uint32_t *clock;
+    bool meta_bound;
+    // per-layer pointers: host-side mirror and device table
+    kvr::LayerPtrs *layers_h;
+    kvr::LayerPtrs *layers_d;
+    bool *layer_bound;
+    size_t resolve_lds;
+};
+
+namespace kvr {
+
+// Launchers (return a hipError_t of the launch).
+hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
+                          const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
+                          int32_t *fill_count, int32_t *status, kvr_stats *stats,
+                          int32_t count_host_bytes, hipStream_t s);
+size_t resolve_lds_bytes(const Shape &sh);
+hipError_t prepare_resolve_kernel();
+
+hipError_t launch_refill(const kvr_ctx *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                         const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
+                         hipStream_t s);
+
+struct GatherTarget {
+    int32_t layer;
+    uint8_t *out;
+};
+hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t n_targets,
+                         int32_t n, const int32_t *req_ids, const uint32_t *loc,
+                         const int32_t *count, int32_t stride, int32_t *status, hipStream_t s);
+
+hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,
+                         const uint8_t *new_rows, int32_t *status, hipStream_t s);
+
+hipError_t launch_init_state(const kvr_ctx *c, hipStream_t s);
+
+hipError_t launch_copy_loc(const kvr_ctx *c, int32_t n, const uint32_t *src, uint32_t *dst,
+                           const int32_t *count, int32_t stride, hipStream_t s);
+
+hipError_t launch_dedup(int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
+                        int32_t *union_count, int32_t *map, hipStream_t s);
+hipError_t prepare_dedup_kernel();
+
+}  // namespace kvr

@@ -1,0 +1,203 @@
+"""Thin ctypes binding of libkvr.so (include/kvr.h).
+
+Argument marshalling only: every entry point forwards raw device pointers,
+sizes and a HIP stream to the C ABI, and raises KvrError on a non-OK return.
+All work on the path runs in the library's HIP kernels; there is no fallback.
+Tensors may be torch tensors (their data_ptr() is passed), plain integer
+addresses, or None for NULL.  The stream defaults to torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvr.so")
+
+OK = 0
+E_ARG = -1
+E_RANGE = -2
+E_CAPACITY = -3
+E_NO_HOST_COPY = -4
+E_HIP = -5
+E_STATE = -6
+
+PLACE_TAIL, PLACE_PAGE, PLACE_HOT, PLACE_INVALID = 0, 1, 2, 3
+LOC_INVALID = 0xFFFFFFFF
+REUSE_SHARED_SOURCE = 0
+REUSE_DISTINCT_PAYLOAD = 1
+
+# Every entry point of include/kvr.h.
+EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
+           "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_gather_rows",
+           "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
+           "kvr_host_alloc", "kvr_host_free")
+
+
+class KvrError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvr error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("history_rows", ctypes.c_int32), ("max_new_rows", ctypes.c_int32),
+                ("page_rows", ctypes.c_int32), ("tail_rows", ctypes.c_int32),
+                ("hot_slots", ctypes.c_int32), ("row_bytes", ctypes.c_int32),
+                ("sel_cap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("pool_pages", ctypes.c_int64)]
+
+
+STATS_FIELDS = ("calls", "tail", "page", "hit", "miss", "fill", "host_bytes", "error")
+
+_lib = None
+
+
+def lib():
+    """Load libkvr.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hierarchical_sparse_kv_resolve_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, U = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "kvr_create": [P, P],
+            "kvr_destroy": [P],
+            "kvr_bind_metadata": [P, P, P, P, P, P, P],
+            "kvr_bind_layer": [P, I, P, P, P, P],
+            "kvr_init_state": [P, P],
+            "kvr_append_rows": [P, I, P, P, P, P],
+            "kvr_resolve_rows": [P, I, P, P, P, I, P, P, P, I, P, P, P],
+            "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
+            "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
+            "kvr_reuse_locations": [P, I, I, I, P, P, P, P, I, P, P, P, P],
+            "kvr_status_summary": [P, I, P],
+            "kvr_host_alloc": [U, P],
+            "kvr_host_free": [P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.kvr_last_error.argtypes = []
+        L.kvr_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):  # numpy array (host memory)
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise KvrError(rc, lib().kvr_last_error().decode())
+    return rc
+
+
+def last_error() -> str:
+    return lib().kvr_last_error().decode()
+
+
+def host_alloc(nbytes: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().kvr_host_alloc(nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def host_free(ptr: int) -> None:
+    _check(lib().kvr_host_free(ptr))
+
+
+def status_summary(status_host) -> tuple[int, int]:
+    """(number of failed requests, index of the first or -1) of a host int32 array."""
+    import numpy as np
+    st = np.ascontiguousarray(status_host, dtype=np.int32)
+    first = ctypes.c_int32()
+    bad = lib().kvr_status_summary(st.ctypes.data, len(st), ctypes.byref(first))
+    if bad < 0:
+        _check(bad)
+    return bad, first.value
+
+
+class Context:
+    """One KV source: n_req requests and n_layers payload layers."""
+
+    def __init__(self, *, n_req, n_layers, history_rows, max_new_rows, page_rows, tail_rows,
+                 hot_slots, row_bytes, sel_cap, pool_pages):
+        self.cfg = Config(n_req, n_layers, history_rows, max_new_rows, page_rows, tail_rows,
+                          hot_slots, row_bytes, sel_cap, 0, pool_pages)
+        h = ctypes.c_void_p()
+        _check(lib().kvr_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self.handle = h.value
+        self._keep = []
+
+    def close(self):
+        if self.handle:
+            lib().kvr_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def bind_metadata(self, L, page_map, host_valid, tag, stamp, clock):
+        _check(lib().kvr_bind_metadata(self.handle, _ptr(L), _ptr(page_map), _ptr(host_valid),
+                                       _ptr(tag), _ptr(stamp), _ptr(clock)))
+
+    def bind_layer(self, layer, tail, pool, hot, host):
+        _check(lib().kvr_bind_layer(self.handle, layer, _ptr(tail), _ptr(pool), _ptr(hot),
+                                    _ptr(host)))
+
+    def init_state(self, stream=None):
+        _check(lib().kvr_init_state(self.handle, _stream(stream)))
+
+    def append_rows(self, n, req_ids, new_rows, status=None, stream=None):
+        _check(lib().kvr_append_rows(self.handle, n, _ptr(req_ids), _ptr(new_rows), _ptr(status),
+                                     _stream(stream)))
+
+    def resolve_rows(self, n, req_ids, sel, sel_count, stride, loc, fills, fill_count, fill_layer,
+                     status, stats=None, stream=None):
+        _check(lib().kvr_resolve_rows(self.handle, n, _ptr(req_ids), _ptr(sel), _ptr(sel_count),
+                                      stride, _ptr(loc), _ptr(fills), _ptr(fill_count), fill_layer,
+                                      _ptr(status), _ptr(stats), _stream(stream)))
+
+    def gather_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None, stream=None):
+        nl = len(layers)
+        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
+        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
+        _check(lib().kvr_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
+                                     _ptr(count), stride, arr_o, _ptr(status), _stream(stream)))
+
+    def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
+        _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),
+                                                 _ptr(union_count), _ptr(map_), _stream(stream)))
+
+    def reuse_locations(self, mode, dst_layer, n, req_ids, src_loc, dst_loc, count, stride,
+                        fills=None, fill_count=None, status=None, stream=None):
+        _check(lib().kvr_reuse_locations(self.handle, mode, dst_layer, n, _ptr(req_ids),
+                                         _ptr(src_loc), _ptr(dst_loc), _ptr(count), stride,
+                                         _ptr(fills), _ptr(fill_count), _ptr(status),
+                                         _stream(stream)))

@@ -1,0 +1,164 @@
+"""Per-decode-step driver of the GPU resolver over one workload.
+
+Owns the device buffers (torch allocates them; pinned host stores come from
+kvr_host_alloc), binds them to a libkvr context and issues, per decode step,
+stream-ordered calls with no host synchronisation:
+
+  append one decoded row per request (all payload layers)
+  for each resolving layer, in order:
+      [verify block]  dedup_verify_selections -> union
+      resolve_rows    (tail / ready page / hot scan / LRU victims; host refill
+                       of payload layer 0)
+      shared indices, distinct payloads: reuse_locations(DISTINCT_PAYLOAD)
+                       replays the fills into every other payload layer, then
+                       one gather_rows over all payload layers
+      one physical source: gather_rows of the source, then
+                       reuse_locations(SHARED_SOURCE) for each Reuse layer
+                       (an alias: no bytes move)
+
+`inputs` supplies shapes and seeded contents (cfg, page_map, host_valid,
+fill_tail/fill_pool/fill_host, new_rows, selections).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import kvr
+
+
+class GpuRun:
+    def __init__(self, inputs, pool_host=None, device: str = "cuda"):
+        import torch
+        self.torch = torch
+        cfg = inputs.cfg
+        self.cfg, self.inputs = cfg, inputs
+        dev = torch.device(device)
+        self.dev = dev
+        n, nl = cfg.n_req, cfg.payload_layers
+        self.n, self.nl = n, nl
+        self.ctx = kvr.Context(n_req=n, n_layers=nl, history_rows=cfg.H,
+                               max_new_rows=inputs.max_new, page_rows=cfg.P, tail_rows=cfg.T,
+                               hot_slots=cfg.B, row_bytes=cfg.R, sel_cap=cfg.sel_cap,
+                               pool_pages=cfg.pool_pages)
+        i32 = torch.int32
+        self.L = torch.empty(n, dtype=i32, device=dev)
+        self.page_map = torch.from_numpy(np.ascontiguousarray(inputs.page_map)).to(dev)
+        self.host_valid = torch.from_numpy(np.ascontiguousarray(inputs.host_valid)).to(dev)
+        self.tag = torch.empty((n, cfg.B), dtype=i32, device=dev)
+        self.stamp = torch.empty((n, cfg.B), dtype=i32, device=dev)   # uint32 bits
+        self.clock = torch.empty(n, dtype=i32, device=dev)            # uint32 bits
+        self.ctx.bind_metadata(self.L, self.page_map, self.host_valid, self.tag, self.stamp,
+                               self.clock)
+        self.tail, self.pool, self.hot, self.host_ptr, self.host = [], [], [], [], []
+        host_bytes = n * inputs.host_rows * cfg.R
+        for l in range(nl):
+            t = np.empty((n, cfg.T, cfg.R), dtype=np.uint8)
+            inputs.fill_tail(l, t)
+            self.tail.append(torch.from_numpy(t).to(dev))
+            if pool_host is not None:
+                p = pool_host[l]
+            else:
+                p = np.empty((cfg.pool_pages, cfg.P, cfg.R), dtype=np.uint8)
+                inputs.fill_pool(l, p)
+            self.pool.append(torch.from_numpy(p).to(dev))
+            self.hot.append(torch.full((n, cfg.B, cfg.R), 0xCD, dtype=torch.uint8, device=dev))
+            ptr = kvr.host_alloc(host_bytes)
+            self.host_ptr.append(ptr)
+            view = np.ctypeslib.as_array((ctypes.c_uint8 * host_bytes).from_address(ptr))
+            view = view.reshape(n, inputs.host_rows, cfg.R)
+            inputs.fill_host(l, view)
+            self.host.append(view)
+            self.ctx.bind_layer(l, self.tail[l] if cfg.T else None,
+                                self.pool[l] if cfg.pool_pages else None, self.hot[l], ptr)
+        self.ctx.init_state()
+        G, cap = cfg.groups, cfg.sel_cap
+        self.loc = [torch.empty((n, cap), dtype=i32, device=dev) for _ in range(G)]
+        self.fills = [torch.empty((n, cfg.B, 2), dtype=i32, device=dev) for _ in range(G)]
+        self.fill_count = [torch.empty(n, dtype=i32, device=dev) for _ in range(G)]
+        self.status = [torch.empty(n, dtype=i32, device=dev) for _ in range(G)]
+        self.append_status = torch.empty(n, dtype=i32, device=dev)
+        self.gather_status = torch.zeros(n, dtype=i32, device=dev)
+        self.stats = torch.zeros(len(kvr.STATS_FIELDS), dtype=torch.int64, device=dev)
+        if cfg.q > 1:
+            self.union = torch.empty((n, cfg.q * cfg.k), dtype=i32, device=dev)
+            self.union_count = torch.empty(n, dtype=i32, device=dev)
+            self.map = torch.empty((n, cfg.q, cfg.k), dtype=i32, device=dev)
+        n_out = nl if cfg.reuse == "distinct" else 1
+        self.outs = [[torch.full((n, cap, cfg.R), 0xEE, dtype=torch.uint8, device=dev)
+                      for _ in range(n_out)] for _ in range(G)]
+        self.sel_dev, self.rows_dev = {}, {}
+
+    def close(self):
+        self.torch.cuda.synchronize()
+        self.ctx.close()
+        for p in self.host_ptr:
+            kvr.host_free(p)
+        self.host_ptr = []
+
+    # ------------------------------------------------------------------
+    def stage(self, steps, sels=None):
+        """Copy the selections and new rows of `steps` to the device (before timing).
+        sels: optional {step: [per-group int32 [n][q][k]]}."""
+        torch = self.torch
+        for s in steps:
+            gs = sels[s] if sels is not None and s in sels else [
+                self.inputs.selections(s, g) for g in range(self.cfg.groups)]
+            self.sel_dev[s] = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(self.dev)
+                               for x in gs]
+            self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
+
+    def step(self, s: int, stream=None):
+        """Enqueue decode step s (staged beforehand).  No host synchronisation."""
+        cfg, ctx, n = self.cfg, self.ctx, self.n
+        ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=stream)
+        for g in range(cfg.groups):
+            sel = self.sel_dev[s][g]
+            k = sel.shape[-1]
+            if cfg.q > 1:
+                ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
+                                            self.map, stream=stream)
+                src, count, stride = self.union, self.union_count, cfg.q * k
+            else:
+                src, count, stride = sel, None, k
+            loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
+            ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, 0, self.status[g],
+                             self.stats, stream=stream)
+            if cfg.reuse == "distinct":
+                for l in range(1, self.nl):
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, l, n, None, loc, None, count,
+                                        stride, fills, fc, stream=stream)
+                ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride, self.outs[g],
+                                self.gather_status, stream=stream)
+            else:
+                ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
+                                self.gather_status, stream=stream)
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, 0, n, None, loc, None, count,
+                                        stride, stream=stream)
+            self._last_stride = stride
+
+    # ------------------------------------------------------------------ read-back (syncs)
+    def state(self) -> dict:
+        self.torch.cuda.synchronize()
+        return {"L": self.L.cpu().numpy(), "tag": self.tag.cpu().numpy(),
+                "stamp": self.stamp.cpu().numpy().view(np.uint32),
+                "clock": self.clock.cpu().numpy().view(np.uint32)}
+
+    def group(self, g: int, with_out: bool = True) -> dict:
+        self.torch.cuda.synchronize()
+        rec = {"loc": self.loc[g].cpu().numpy().view(np.uint32),
+               "fills": self.fills[g].cpu().numpy(),
+               "fill_count": self.fill_count[g].cpu().numpy(),
+               "status": self.status[g].cpu().numpy()}
+        if self.cfg.q > 1:
+            rec.update(union=self.union.cpu().numpy(), union_count=self.union_count.cpu().numpy(),
+                       map=self.map.cpu().numpy())
+        if with_out:
+            rec["out"] = [o.cpu().numpy() for o in self.outs[g]]
+        return rec
+
+    def stats_dict(self) -> dict:
+        vals = self.stats.cpu().numpy().astype(np.uint64)
+        return dict(zip(kvr.STATS_FIELDS, (int(v) for v in vals)))

@@ -1,0 +1,231 @@
+/*
+ * kvr.h - C ABI of the MI355X (gfx950) per-decode-step sparse KV row resolver.
+ *
+ * The method is the resolver of "Adaptive DHiSparse: Speculative Decoding over
+ * a Load-Adaptive KV Hierarchy" (section "How it works"):
+ *   - Memory split: every (request, KV source) owns a fixed hot cache of B
+ *     rows, a mutable tail and metadata; complete pages of imported history can
+ *     also sit, ready, in an optional pool shared by all requests.
+ *   - Resolution: each selected row is looked up, in order and stopping at the
+ *     first hit, in (1) the tail and the ready optional-history page map,
+ *     (2) the hot cache, scanning at most B slots, with LRU replacement,
+ *     (3) pinned host memory, copied into the hot cache.
+ *   - Speculative state: verification queries share missing-row retrieval.
+ *   - Model-specific reuse: Reuse layers inherit a location vector when they
+ *     share one physical KV source; layers that share sparse indices but own
+ *     distinct payloads fetch the same positions for their own payload.
+ *
+ * One context serves one KV source: n_req requests and n_layers payload
+ * layers that share the source's metadata (history length, page map, hot-cache
+ * tags and stamps).
+ *
+ * Conventions
+ *   - Every buffer is caller-owned.  Pointers marked (device) are device
+ *     memory; (host) is ordinary host memory read during the call; (pinned) is
+ *     page-locked host memory from hipHostMalloc (for example kvr_host_alloc or
+ *     a pinned torch tensor), which kernels read and write directly over the
+ *     host link.  The library keeps bound pointers until kvr_destroy and never
+ *     frees them.
+ *   - Calls that take a stream enqueue work on it (a hipStream_t; NULL is the
+ *     default stream) and return without waiting for the device.  They never
+ *     synchronise the host and allocate nothing.  Their return value reports
+ *     argument errors only.
+ *   - Data-dependent errors (a selected row outside [0, L), more distinct
+ *     pending rows than B, a missing row without a host copy) are written per
+ *     request into a device status array, stream-ordered.  A request that fails
+ *     changes nothing: L, tags, stamps, clock and hot payload stay as they were
+ *     and its locations read KVR_LOC_INVALID.  The other requests of the call
+ *     complete normally.
+ *   - Return codes are kvr_status values; kvr_last_error() gives a message for
+ *     the calling thread's last failure.  No C++ exception leaves the library.
+ *
+ * Location word (uint32): bits 31..30 give the place (kvr_place), bits 29..0
+ * the index in it: the tail ring slot (pos mod T), the optional-pool row
+ * (physical page * P + pos mod P) or the hot-cache slot.
+ */
+#ifndef KVR_H
+#define KVR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvr_status {
+    KVR_OK = 0,
+    KVR_E_ARG = -1,          /* bad argument, shape or unbound buffer            */
+    KVR_E_RANGE = -2,        /* selected row outside [0, L), or a bad location   */
+    KVR_E_CAPACITY = -3,     /* more distinct pending rows than B; history full  */
+    KVR_E_NO_HOST_COPY = -4, /* a missing row is neither on device nor on host   */
+    KVR_E_HIP = -5,          /* the HIP runtime reported an error               */
+    KVR_E_STATE = -6,        /* the LRU clock would wrap                         */
+} kvr_status;
+
+typedef enum kvr_place {
+    KVR_PLACE_TAIL = 0,
+    KVR_PLACE_PAGE = 1,
+    KVR_PLACE_HOT = 2,
+    KVR_PLACE_INVALID = 3,
+} kvr_place;
+
+#define KVR_LOC_INVALID 0xFFFFFFFFu
+
+typedef enum kvr_reuse_mode {
+    /* Reuse layers of one physical KV source: the location vector is inherited
+     * as is (dst_loc NULL = alias, zero bytes moved; else a copy of it). */
+    KVR_REUSE_SHARED_SOURCE = 0,
+    /* Shared indices, distinct per-layer payloads: the rows filled from host
+     * for one layer are fetched into the same hot slots of dst_layer from
+     * dst_layer's host store; dst_loc (optional) receives a copy of src_loc. */
+    KVR_REUSE_DISTINCT_PAYLOAD = 1,
+} kvr_reuse_mode;
+
+/* Shape of one KV source.  Limits: 1 <= hot_slots <= 8192,
+ * 1 <= sel_cap <= 8192, row_bytes a positive multiple of 16,
+ * pool_pages * page_rows < 2^30, history_rows + max_new_rows < 2^31. */
+typedef struct kvr_config {
+    int32_t n_req;        /* requests of the source                           */
+    int32_t n_layers;     /* payload layers sharing the source's metadata     */
+    int32_t history_rows; /* H: imported history rows per request             */
+    int32_t max_new_rows; /* decoded rows a request may append                */
+    int32_t page_rows;    /* P: rows per optional-history page                */
+    int32_t tail_rows;    /* T: rows in the mutable tail ring (0 = no tail)   */
+    int32_t hot_slots;    /* B: hot-cache slots per request                   */
+    int32_t row_bytes;    /* R: bytes per row (opaque payload)                */
+    int32_t sel_cap;      /* most selection entries one request passes to one
+                             resolve call (the union capacity for verify)     */
+    int32_t reserved;     /* must be 0                                        */
+    int64_t pool_pages;   /* pages in the global optional pool, per layer     */
+} kvr_config;
+
+/* One host refill: `row` was copied into hot slot `slot`. */
+typedef struct kvr_fill {
+    int32_t row;
+    int32_t slot;
+} kvr_fill;
+
+/* Resolution counters, added to (device atomics) by every resolve call.
+ * tail/page/hit/miss count selection entries by where they were found; fill
+ * counts distinct rows copied from host and host_bytes their bytes. */
+typedef struct kvr_stats {
+    uint64_t calls, tail, page, hit, miss, fill, host_bytes, error;
+} kvr_stats;
+
+typedef struct kvr_ctx kvr_ctx;
+
+/* Validate `cfg` and create a context on the current HIP device.  Allocates
+ * only a small device table of layer pointers.  *out is NULL on failure. */
+int kvr_create(const kvr_config *cfg, kvr_ctx **out);
+
+/* Free the context (not the bound buffers).  NULL is accepted. */
+int kvr_destroy(kvr_ctx *ctx);
+
+/* Message for the calling thread's last non-OK return ("" if none). */
+const char *kvr_last_error(void);
+
+/* Bind the source's metadata (all device):
+ *   L         int32  [n_req]              rows held: H + decoded rows
+ *   page_map  int32  [n_req][ceil(H/P)]   physical page of a ready complete
+ *                                          page, else -1 (a trailing partial
+ *                                          page is never ready)
+ *   host_valid uint8 [n_req][ceil(H/P)]   1 if the imported page has a host copy
+ *   tag       int32  [n_req][B]           row held by a hot slot, -1 = empty
+ *   stamp     uint32 [n_req][B]           LRU stamp of a hot slot
+ *   clock     uint32 [n_req]              last LRU tick of the request */
+int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, const int32_t *page_map, const uint8_t *host_valid,
+                      int32_t *tag, uint32_t *stamp, uint32_t *clock);
+
+/* Bind one payload layer:
+ *   tail (device) [n_req][T][R], pool (device) [pool_pages][P][R] (read only),
+ *   hot (device) [n_req][B][R], host (pinned) [n_req][H + max_new][R].
+ * tail may be NULL when T = 0 and pool when pool_pages = 0. */
+int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, const void *pool, void *hot,
+                   void *host);
+
+/* Fresh admission: L = H, every tag -1, every stamp 0, every clock 0. */
+int kvr_init_state(kvr_ctx *ctx, void *stream);
+
+/* Append one decoded row to each listed request, for every layer: the row
+ * goes to tail slot L mod T and, written through, to host row L; then L += 1.
+ * Decoded rows never enter optional pages (section "Limits": they follow
+ * hot-cache rules), which is why they get a host copy.
+ *   req_ids  (device) int32 [n] or NULL (= 0..n-1); distinct
+ *   new_rows (device) [n_layers][n][R]
+ *   status   (device) int32 [n] or NULL: KVR_OK, or KVR_E_CAPACITY when the
+ *            request already holds H + max_new rows (nothing written). */
+int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                    int32_t *status, void *stream);
+
+/* Resolve one selection per listed request ("Resolution", steps 1-3).
+ *   sel       (device) int32 [n][stride], rows of request i in sel[i][0..cnt)
+ *   sel_count (device) int32 [n] or NULL (= stride); 0 <= cnt <= stride <= sel_cap
+ *   loc       (device) uint32 [n][stride] out; entries >= cnt untouched
+ *   fills     (device) kvr_fill [n][B] out: the rows copied from host, by
+ *             ascending row; fill_count (device) int32 [n] out
+ *   fill_layer payload layer refilled from host now, or -1 for none (the
+ *             fills can be replayed per layer with kvr_reuse_locations)
+ *   status    (device) int32 [n] out, required
+ *   stats     (device) kvr_stats or NULL, added to
+ * Per request, with now = clock + 1 (one tick per call):
+ *   1. a row in [max(0, L - T), L) is in the tail; else a row of a ready
+ *      complete page is in the optional pool; else it is pending;
+ *   2. each distinct pending row is looked for among the B tags; a hit
+ *      stamps its slot with now;
+ *   3. misses, by ascending row, take the slots not hit in this call with the
+ *      smallest (stamp, slot), which get the row's tag and stamp now, and the
+ *      host copy is fetched into them.
+ * Repeated rows in one selection share one location. */
+int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *sel,
+                     const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
+                     int32_t *fill_count, int32_t fill_layer, int32_t *status, kvr_stats *stats,
+                     void *stream);
+
+/* Gather resolved rows into contiguous per-request buffers, for several
+ * payload layers sharing one location vector:
+ *   out[l] (device) [n][stride][R] for layers[l]; row j < cnt of request i is
+ *   the R bytes at loc[i][j] in that layer.  Invalid locations leave the row
+ *   untouched.
+ *   layers (host) int32 [n_layers]; out (host) array of n_layers device pointers
+ *   loc (device) uint32 [n][stride]; count (device) int32 [n] or NULL (= stride)
+ *   status (device) int32 [n] or NULL: set to KVR_E_RANGE for a request with a
+ *   location outside its place, otherwise not written (clear it beforehand). */
+int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                    const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
+                    int32_t stride, void *const *out, int32_t *status, void *stream);
+
+/* Verification block dedup ("Speculative state": queries share missing-row
+ * retrieval).  Per request: union_rows[i][0..u) = the distinct rows of the q
+ * selections, ascending; map[i][qi][j] = index of sel[i][qi][j] in it.
+ *   sel (device) int32 [n][q][k]; union_rows (device) int32 [n][q*k];
+ *   union_count (device) int32 [n]; map (device) int32 [n][q][k].
+ *   Requires q * k <= 16384.  The union is then resolved once. */
+int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,
+                                int32_t *union_rows, int32_t *union_count, int32_t *map,
+                                void *stream);
+
+/* Location reuse across layers ("Model-specific reuse"); see kvr_reuse_mode.
+ *   src_loc/dst_loc (device) uint32 [n][stride]; count (device) int32 [n] or NULL
+ *   fills/fill_count (device): from the resolve call (DISTINCT_PAYLOAD only)
+ *   status (device) int32 [n] or NULL: set to KVR_E_RANGE if a fill names a
+ *   row or slot out of range, otherwise not written. */
+int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n,
+                        const int32_t *req_ids, const uint32_t *src_loc, uint32_t *dst_loc,
+                        const int32_t *count, int32_t stride, const kvr_fill *fills,
+                        const int32_t *fill_count, int32_t *status, void *stream);
+
+/* Host helper, after the caller has synchronised and copied status to host:
+ * number of failed requests; *first_bad = index of the first (or -1). */
+int kvr_status_summary(const int32_t *status, int32_t n, int32_t *first_bad);
+
+/* Page-locked, device-mapped host memory for host stores (hipHostMalloc).
+ * Returns KVR_E_HIP on failure. */
+int kvr_host_alloc(size_t bytes, void **out);
+int kvr_host_free(void *ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVR_H */

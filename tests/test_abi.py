@@ -1,0 +1,58 @@
+"""The C ABI library loads and exports every call its header declares; host-side
+argument checks work without a GPU (no compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from hierarchical_sparse_kv_resolve_amd import kvr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    text = open(os.path.join(ROOT, "include", "kvr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_lifecycle():
+    names = declared()
+    for n in ("kvr_resolve_rows", "kvr_gather_rows", "kvr_dedup_verify_selections",
+              "kvr_reuse_locations", "kvr_append_rows", "kvr_create", "kvr_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kvr.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing
+    assert sorted(kvr.EXPORTS) == declared()
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("hot_slots", 0, "hot_slots"), ("hot_slots", 8193, "hot_slots"),
+    ("row_bytes", 24, "row_bytes"), ("sel_cap", 0, "sel_cap"), ("page_rows", 0, "page_rows"),
+    ("pool_pages", 1 << 30, "pool_pages"), ("n_req", 0, "n_req"), ("tail_rows", -1, "tail_rows"),
+])
+def test_create_rejects_bad_shapes(field, value, msg):
+    good = dict(n_req=2, n_layers=1, history_rows=100, max_new_rows=4, page_rows=8, tail_rows=4,
+                hot_slots=16, row_bytes=32, sel_cap=16, pool_pages=3)
+    good[field] = value
+    with pytest.raises(kvr.KvrError) as e:
+        kvr.Context(**good)
+    assert e.value.code == kvr.E_ARG and msg in str(e.value)
+
+
+def test_null_context_and_status_summary():
+    lib = kvr.lib()
+    assert lib.kvr_resolve_rows(None, 0, None, None, None, 0, None, None, None, -1, None, None,
+                                None) == kvr.E_ARG
+    assert "null context" in kvr.last_error()
+    assert kvr.status_summary(np.array([0, 0, -2, 0, -3], dtype=np.int32)) == (2, 2)
+    assert kvr.status_summary(np.zeros(3, dtype=np.int32)) == (0, -1)
+    assert lib.kvr_destroy(None) == kvr.OK
