@@ -1,0 +1,273 @@
+"""Benchmark of the per-decode-step sparse KV row resolver on one MI355X.
+
+A step is one pass of the whole resolver path over one batch: append one
+decoded row per request, then per resolving layer: (verify-block dedup),
+resolve (tail / ready page / hot-cache scan / LRU victims), host refill of
+the missing rows, per-layer replays for layers that share indices with
+distinct payloads, and the multi-layer gather into contiguous buffers.
+Inputs (selections, new rows, payload) are seeded synthetic data, staged
+in HBM and pinned host memory before the timed region.
+
+Prints one JSON line.  `value` is selected rows resolved+gathered per
+second: (request, payload layer, selected row) entries written by the
+gather; rows of layers that only inherit a location vector are not counted.
+
+  python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import contextlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=28)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+class EventTimer:
+    """Brackets named calls with HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    @contextlib.contextmanager
+    def __call__(self, name):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name):
+        ps = self.pairs.get(name, [])
+        if not ps:
+            return None
+        return float(np.mean([a.elapsed_time(b) for a, b in ps]))
+
+    def count(self, name):
+        return len(self.pairs.get(name, []))
+
+
+def rows_per_group(inputs, steps):
+    """Per (step, group): rows resolved by the call (union size for verify)."""
+    cfg = inputs.cfg
+    out = {}
+    for s in steps:
+        for g in range(cfg.groups):
+            sel = inputs.selections(s, g)
+            if cfg.q > 1:
+                out[(s, g)] = sum(len(np.unique(sel[r])) for r in range(cfg.n_req))
+            else:
+                out[(s, g)] = sel.shape[0] * sel.shape[2]
+    return out
+
+
+def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0):
+    """The oracle as it stands, on this host's cores, over the same decode
+    steps from a fresh state; the pass is repeated (state restored) until at
+    least `min_s` seconds of work, and stops early at `budget_s`."""
+    from oracle.runner import OracleRun
+    from synth import Inputs
+    inputs = Inputs(cfg, max_new=total_steps)
+    run = OracleRun(inputs)
+    src = run.src
+    snap = src.snapshot()
+    sels = {s: [inputs.selections(s, g) for g in range(cfg.groups)] for s in range(total_steps)}
+    n_out = cfg.payload_layers if cfg.reuse == "distinct" else 1
+    rows = 0
+    spent = 0.0
+    passes = 0
+    steps_done = 0
+    while spent < min_s and spent < budget_s:
+        for name in ("L", "tag", "stamp", "clock"):
+            np.copyto(getattr(src, name), snap[name])
+        for l in range(src.n_layers):
+            np.copyto(src.hot[l], snap["hot"][l])
+            np.copyto(src.tail[l], snap["tail"][l])
+        t0 = time.perf_counter()
+        for s in range(total_steps):
+            res = run.step(s, sels=sels[s])
+            for rec in res["groups"]:
+                cnt = rec["count"]
+                per = int(cnt.sum()) if cnt is not None else rec["loc"].size
+                rows += per * n_out
+            steps_done += 1
+            if spent + time.perf_counter() - t0 > budget_s:
+                break
+        spent += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(rows / spent, 1), "unit": "rows/s", "cores": int(src.threads),
+            "kind": "oracle",
+            "sample": f"{cfg.name}: {passes} pass(es) over decode steps 0..{total_steps - 1} of all "
+                      f"{cfg.n_req} requests from a fresh state, {steps_done} steps, "
+                      f"{spent:.1f} s of oracle time"}
+
+
+def host_link_gbs(torch, nbytes=1 << 30, reps=5):
+    """Pinned host -> device copy rate (hipMemcpyAsync through torch)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the resolver keeps each request's state on "
+              "one device and this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    from hierarchical_sparse_kv_resolve_amd.runner import GpuRun
+    from synth import FULL, Inputs
+
+    c = int(args.workload[1])
+    K, W = args.steps, args.warmup
+    total = K + W
+    cfg = FULL[c].with_(steps=total)
+    inputs = Inputs(cfg, max_new=total)
+    log(f"workload {cfg.name}: staging {total} steps")
+    gpu = GpuRun(inputs)
+    gpu.stage(range(total))
+    log("staged; warming up")
+    counts = rows_per_group(inputs, range(W, total))
+    timer = EventTimer(torch)
+    for s in range(W):
+        gpu.step(s)
+    torch.cuda.synchronize()
+    stats_before = gpu.stats_dict()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(W, total):
+        gpu.step(s, timer=timer)
+    end.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    log(f"timed {K} steps in {wall_s * 1e3:.3f} ms")
+    gpu_ms = start.elapsed_time(end)
+
+    # every request of every timed call must have resolved
+    for g in range(cfg.groups):
+        st = gpu.status[g].cpu().numpy()
+        if (st != 0).any():
+            raise SystemExit(f"resolve failed: status {st.tolist()}")
+    if (gpu.gather_status.cpu().numpy() != 0).any() or (gpu.append_status.cpu().numpy() != 0).any():
+        raise SystemExit("gather or append reported an error")
+    # spot check of the last step against the payload closed form
+    from synth import payload_np
+    last = total - 1
+    rec = gpu.group(cfg.groups - 1)
+    sel = inputs.selections(last, cfg.groups - 1)
+    rows_src = rec["union"] if cfg.q > 1 else sel[:, 0, :]
+    for r in range(0, cfg.n_req, max(1, cfg.n_req // 4)):
+        j = np.arange(0, 64)
+        for l, out in enumerate(rec["out"]):
+            if not np.array_equal(out[r, j], payload_np(l, r, rows_src[r, j], cfg.R, cfg.seed)):
+                raise SystemExit("gathered bytes differ from the payload closed form")
+
+    n_out = cfg.payload_layers if cfg.reuse == "distinct" else 1
+    rows_total = sum(counts.values()) * n_out
+    value = rows_total / wall_s
+
+    # gather roofline: algorithmic bytes per launch = rows * (R read + R write) per
+    # payload layer + one 4-byte location word per row
+    gather_calls = timer.count("gather")
+    bytes_gather = sum(v * (2 * cfg.R * n_out + 4) for v in counts.values()) / max(1, gather_calls)
+    g_ms = timer.mean_ms("gather")
+    achieved = bytes_gather / (g_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gather_kernel", "bytes_per_launch": int(bytes_gather),
+                "launch_us": round(g_ms * 1e3, 2)}
+
+    stats_all = gpu.stats_dict()
+    stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}
+    found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
+    split = {"step1_tail_or_page": round((stats["tail"] + stats["page"]) / found, 4),
+             "step2_hot_hit": round(stats["hit"] / found, 4),
+             "step3_host": round(stats["miss"] / found, 4)}
+    per_call_us = {name: round(timer.mean_ms(name) * 1e3, 2)
+                   for name in ("append", "dedup", "resolve", "refill", "replay", "gather")
+                   if timer.count(name)}
+    # host refill path: bytes each refill/replay call reads over the host link
+    n_fill_calls = timer.count("refill")
+    host_bytes_per_call = stats["fill"] * cfg.R / max(1, n_fill_calls)
+    fill_ms = [timer.mean_ms(nm) for nm in ("refill", "replay") if timer.count(nm)]
+    fill_us = float(np.mean(fill_ms)) * 1e3 if fill_ms else None
+    link = host_link_gbs(torch)
+    refill_gbs = host_bytes_per_call / (fill_us * 1e-6) / 1e9 if fill_us else None
+    host_link = {"refill_gbs": round(refill_gbs, 1) if refill_gbs else None,
+                 "pinned_h2d_copy_gbs": round(link, 1),
+                 "frac": round(refill_gbs / link, 4) if refill_gbs else None,
+                 "host_bytes_per_call": int(host_bytes_per_call),
+                 "call_us": round(fill_us, 2) if fill_us else None}
+    line = {
+        "metric": "selected rows resolved+gathered/sec and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall_s * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": cfg.name, "n_req": cfg.n_req, "history_rows": cfg.H,
+                   "row_bytes": cfg.R, "page_rows": cfg.P, "tail_rows": cfg.T,
+                   "ready_frac": cfg.ready_frac, "hot_slots": cfg.B, "top_k": cfg.k,
+                   "verify_queries": cfg.q, "payload_layers": cfg.payload_layers,
+                   "model_layers": cfg.model_layers, "resolving_layers": cfg.groups,
+                   "selection": cfg.sel, "zipf_s": cfg.zipf_s, "parallelism": "none"},
+        "roofline": roofline,
+        "gpu_ms_per_step": round(gpu_ms / K, 4),
+        "per_call_us": per_call_us,
+        "resolution_split": split,
+        "host_link": host_link,
+    }
+    gpu.close()
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        line["cpu_baseline"] = cpu_baseline(FULL[c], total, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,21 @@ import numpy as np
 from . import kvr
 
 
+class _NoTimer:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO = _NoTimer()
+
+
+def _no_timer(name):
+    return _NO
+
+
 class GpuRun:
     def __init__(self, inputs, pool_host=None, device: str = "cuda"):
         import torch
@@ -109,35 +124,51 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, stream=None):
-        """Enqueue decode step s (staged beforehand).  No host synchronisation."""
+    def step(self, s: int, stream=None, timer=None):
+        """Enqueue decode step s (staged beforehand).  No host synchronisation.
+
+        `timer(name)` may return a context manager that brackets a call with
+        events on the stream (used by the benchmark); with a timer the host
+        refill of layer 0 is issued as its own replay call so it can be timed
+        apart from the resolve (the result is the same)."""
         cfg, ctx, n = self.cfg, self.ctx, self.n
-        ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=stream)
+        tm = timer or _no_timer
+        with tm("append"):
+            ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=stream)
         for g in range(cfg.groups):
             sel = self.sel_dev[s][g]
             k = sel.shape[-1]
             if cfg.q > 1:
-                ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
-                                            self.map, stream=stream)
+                with tm("dedup"):
+                    ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
+                                                self.map, stream=stream)
                 src, count, stride = self.union, self.union_count, cfg.q * k
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, 0, self.status[g],
-                             self.stats, stream=stream)
+            fill_layer = -1 if timer else 0
+            with tm("resolve"):
+                ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
+                                 self.status[g], self.stats, stream=stream)
+            if timer:
+                with tm("refill"):
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, 0, n, None, loc, None, count,
+                                        stride, fills, fc, stream=stream)
             if cfg.reuse == "distinct":
                 for l in range(1, self.nl):
-                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, l, n, None, loc, None, count,
-                                        stride, fills, fc, stream=stream)
-                ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride, self.outs[g],
-                                self.gather_status, stream=stream)
+                    with tm("replay"):
+                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, l, n, None, loc, None,
+                                            count, stride, fills, fc, stream=stream)
+                with tm("gather"):
+                    ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
+                                    self.outs[g], self.gather_status, stream=stream)
             else:
-                ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
-                                self.gather_status, stream=stream)
+                with tm("gather"):
+                    ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
+                                    self.gather_status, stream=stream)
                 for _ in range(1, cfg.layers_per_group):
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, 0, n, None, loc, None, count,
                                         stride, stream=stream)
-            self._last_stride = stride
 
     # ------------------------------------------------------------------ read-back (syncs)
     def state(self) -> dict:

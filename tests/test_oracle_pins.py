@@ -378,3 +378,19 @@ def test_reduced_workload_invariants_and_bytes(c):
                 for l, out in enumerate(rec["out"]):
                     assert np.array_equal(out[r, :n], payload_np(l, r, pos, cfg.R, cfg.seed))
         assert (src.check() == 0).all()
+
+
+# ----------------------------------------------------------------- regression fixture
+
+
+def test_golden_regression_fixture():
+    """The oracle still produces the stored trace (tests/golden/make_golden.py)."""
+    import json
+    import os
+
+    from tests.golden.make_golden import run
+    path = os.path.join(os.path.dirname(__file__), "golden", "lru_trace_small.json")
+    fx = json.load(open(path))
+    assert run(fx) == fx["expected"]
+    statuses = {e["status"] for e in fx["expected"]}
+    assert orc.E_CAPACITY in statuses and orc.OK in statuses
