@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="issue the timed steps eagerly instead of replaying one HIP graph")
+    ap.add_argument("--prefetch-groups", type=int, default=2,
+                    help="layer groups whose host fills overlap earlier gathers (0 = off)")
     return ap.parse_args()
 
 
@@ -55,12 +59,13 @@ class EventTimer:
         self.pairs = {}
 
     @contextlib.contextmanager
-    def __call__(self, name):
+    def __call__(self, name, stream=None):
+        stream = stream or self.torch.cuda.current_stream()
         a = self.torch.cuda.Event(enable_timing=True)
         b = self.torch.cuda.Event(enable_timing=True)
-        a.record()
+        a.record(stream)
         yield
-        b.record()
+        b.record(stream)
         self.pairs.setdefault(name, []).append((a, b))
 
     def mean_ms(self, name):
@@ -171,18 +176,37 @@ def main():
     log("staged; warming up")
     counts = rows_per_group(inputs, range(W, total))
     timer = EventTimer(torch)
+    pg = args.prefetch_groups
     for s in range(W):
-        gpu.step(s)
+        gpu.step(s, prefetch_groups=pg)
     torch.cuda.synchronize()
+    snap = gpu.snapshot()
     stats_before = gpu.stats_dict()
 
+    # Pass 1 (eager, same steps): HIP events around every call give the
+    # per-kernel durations (events cannot be recorded inside a graph).
+    for s in range(W, total):
+        gpu.step(s, timer=timer, prefetch_groups=pg)
+    torch.cuda.synchronize()
+    if not args.no_graph:
+        gpu.restore(snap)
+        graph = gpu.capture(range(W, total), prefetch_groups=pg)
+        torch.cuda.synchronize()
+        log("captured the timed steps into one graph")
+
+    # Pass 2 (timed): the K decode steps from the same starting state.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        gpu.restore(snap)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for s in range(W, total):
-        gpu.step(s, timer=timer)
+    if args.no_graph:
+        for s in range(W, total):
+            gpu.step(s, prefetch_groups=pg)
+    else:
+        graph.replay()
     end.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -222,7 +246,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": "gather_kernel", "bytes_per_launch": int(bytes_gather),
-                "launch_us": round(g_ms * 1e3, 2)}
+                "launch_us": round(g_ms * 1e3, 2),
+                "timing": "HIP events around each gather launch in an eager pass over the "
+                          "same timed steps from the same starting state"}
 
     stats_all = gpu.stats_dict()
     stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}
@@ -233,24 +259,26 @@ def main():
     per_call_us = {name: round(timer.mean_ms(name) * 1e3, 2)
                    for name in ("append", "dedup", "resolve", "refill", "replay", "gather")
                    if timer.count(name)}
-    # host refill path: bytes each refill/replay call reads over the host link
-    n_fill_calls = timer.count("refill")
-    host_bytes_per_call = stats["fill"] * cfg.R / max(1, n_fill_calls)
-    fill_ms = [timer.mean_ms(nm) for nm in ("refill", "replay") if timer.count(nm)]
-    fill_us = float(np.mean(fill_ms)) * 1e3 if fill_ms else None
+    # host refill path: every fill is fetched once per payload layer (all layers
+    # replay the fills for shared indices with distinct payloads)
+    fill_layers = cfg.payload_layers if cfg.reuse == "distinct" else 1
+    host_bytes = stats["fill"] * cfg.R * fill_layers
+    fill_calls = timer.pairs.get("refill", [])
+    fill_s = sum(a.elapsed_time(b) for a, b in fill_calls) * 1e-3
     link = host_link_gbs(torch)
-    refill_gbs = host_bytes_per_call / (fill_us * 1e-6) / 1e9 if fill_us else None
+    refill_gbs = host_bytes / fill_s / 1e9 if fill_s > 0 else None
     host_link = {"refill_gbs": round(refill_gbs, 1) if refill_gbs else None,
                  "pinned_h2d_copy_gbs": round(link, 1),
                  "frac": round(refill_gbs / link, 4) if refill_gbs else None,
-                 "host_bytes_per_call": int(host_bytes_per_call),
-                 "call_us": round(fill_us, 2) if fill_us else None}
+                 "host_bytes_per_step": int(host_bytes / K),
+                 "refill_calls_per_step": len(fill_calls) / K}
     line = {
         "metric": "selected rows resolved+gathered/sec and achieved HBM GB/s (% of peak), 1 GPU",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(wall_s * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-        "config": {"workload": cfg.name, "n_req": cfg.n_req, "history_rows": cfg.H,
+        "config": {"workload": cfg.name, "prefetch_groups": args.prefetch_groups,
+                   "launch": "eager" if args.no_graph else "hip_graph", "n_req": cfg.n_req, "history_rows": cfg.H,
                    "row_bytes": cfg.R, "page_rows": cfg.P, "tail_rows": cfg.T,
                    "ready_frac": cfg.ready_frac, "hot_slots": cfg.B, "top_k": cfg.k,
                    "verify_queries": cfg.q, "payload_layers": cfg.payload_layers,

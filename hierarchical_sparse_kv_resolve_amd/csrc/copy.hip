@@ -123,18 +123,21 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 struct RefillArgs {
     Shape sh;
     TileShape ts;
-    LayerPtrs lp;
+    uint8_t *hot[kGatherLayersPerLaunch];
+    const uint8_t *host[kGatherLayersPerLaunch];
     const int32_t *req_ids;
     const kvr_fill *fills;
     const int32_t *fill_count;
     int32_t *status;
 };
 
+// grid: (tiles of B fill rows, requests, layers)
 __global__ __launch_bounds__(NT) void refill_kernel(RefillArgs a)
 {
     __shared__ const uint8_t *sSrc[kMaxTileRows];
     __shared__ uint8_t *sDst[kMaxTileRows];
     const int i = blockIdx.y;
+    const int t = blockIdx.z;
     const int r = a.req_ids ? a.req_ids[i] : i;
     int fc = a.fill_count[i];
     fc = fc < 0 ? 0 : (fc > a.sh.B ? a.sh.B : fc);
@@ -146,8 +149,8 @@ __global__ __launch_bounds__(NT) void refill_kernel(RefillArgs a)
     if ((int)threadIdx.x < nrows) {
         const kvr_fill f = a.fills[(int64_t)i * a.sh.B + j0 + threadIdx.x];
         const bool ok = f.row >= 0 && (int64_t)f.row < a.sh.host_rows && f.slot >= 0 && f.slot < a.sh.B;
-        sSrc[threadIdx.x] = ok ? a.lp.host + ((int64_t)r * a.sh.host_rows + f.row) * R : nullptr;
-        sDst[threadIdx.x] = ok ? a.lp.hot + ((int64_t)r * a.sh.B + f.slot) * R : nullptr;
+        sSrc[threadIdx.x] = ok ? a.host[t] + ((int64_t)r * a.sh.host_rows + f.row) * R : nullptr;
+        sDst[threadIdx.x] = ok ? a.hot[t] + ((int64_t)r * a.sh.B + f.slot) * R : nullptr;
         if (!ok && a.status)
             a.status[i] = KVR_E_RANGE;
     }
@@ -163,11 +166,11 @@ __global__ __launch_bounds__(NT) void refill_kernel(RefillArgs a)
             dsts[u] = nullptr;
             if (c < total) {
                 const int row = (int)(((uint64_t)(uint32_t)c * a.ts.magic) >> 32);
-                const uint8_t *s = sSrc[row];
-                if (s) {
+                const uint8_t *src = sSrc[row];
+                if (src) {
                     const int off = (c - row * C) * 16;
                     dsts[u] = sDst[row] + off;
-                    load_chunk(v[u], s + off);
+                    load_chunk(v[u], src + off);
                 }
             }
         }
@@ -305,21 +308,30 @@ hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t 
     return hipSuccess;
 }
 
-hipError_t launch_refill(const kvr_ctx *c, int32_t layer, int32_t n, const int32_t *req_ids,
-                         const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
-                         hipStream_t s)
+hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_layers, int32_t n,
+                         const int32_t *req_ids, const kvr_fill *fills, const int32_t *fill_count,
+                         int32_t *status, hipStream_t s)
 {
     RefillArgs a;
     a.sh = c->shape;
     a.ts = tile_for(c->shape);
-    a.lp = c->layers_h[layer];
     a.req_ids = req_ids;
     a.fills = fills;
     a.fill_count = fill_count;
     a.status = status;
-    dim3 grid((c->shape.B + a.ts.rows - 1) / a.ts.rows, n);
-    hipLaunchKernelGGL(refill_kernel, grid, dim3(NT), 0, s, a);
-    return hipGetLastError();
+    for (int32_t t0 = 0; t0 < n_layers; t0 += kGatherLayersPerLaunch) {
+        const int nt = n_layers - t0 < kGatherLayersPerLaunch ? n_layers - t0 : kGatherLayersPerLaunch;
+        for (int t = 0; t < nt; ++t) {
+            a.hot[t] = c->layers_h[layers[t0 + t]].hot;
+            a.host[t] = c->layers_h[layers[t0 + t]].host;
+        }
+        dim3 grid((c->shape.B + a.ts.rows - 1) / a.ts.rows, n, nt);
+        hipLaunchKernelGGL(refill_kernel, grid, dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,

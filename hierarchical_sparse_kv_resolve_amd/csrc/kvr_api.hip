@@ -281,7 +281,7 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
     if (e != hipSuccess)
         return hip_fail(e, "resolve launch");
     if (fill_layer >= 0) {
-        e = kvr::launch_refill(ctx, fill_layer, n, req_ids, fills, fill_count, nullptr, s);
+        e = kvr::launch_refill(ctx, &fill_layer, 1, n, req_ids, fills, fill_count, nullptr, s);
         if (e != hipSuccess)
             return hip_fail(e, "refill launch");
     }
@@ -352,10 +352,11 @@ int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, c
     return e == hipSuccess ? ok() : hip_fail(e, "dedup launch");
 }
 
-int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n,
-                        const int32_t *req_ids, const uint32_t *src_loc, uint32_t *dst_loc,
-                        const int32_t *count, int32_t stride, const kvr_fill *fills,
-                        const int32_t *fill_count, int32_t *status, void *stream)
+int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *dst_layers,
+                        int32_t n, const int32_t *req_ids, const uint32_t *src_loc,
+                        uint32_t *dst_loc, const int32_t *count, int32_t stride,
+                        const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
+                        void *stream)
 {
     if (int rc = check_ctx(ctx, false))
         return rc;
@@ -368,9 +369,12 @@ int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n
     if (dst_loc && !src_loc && stride > 0 && n > 0)
         return fail(KVR_E_ARG, "src_loc is required to copy locations");
     if (mode == KVR_REUSE_DISTINCT_PAYLOAD) {
-        if (int rc = check_layer(ctx, dst_layer))
-            return rc;
-        if (n > 0 && (!fills || !fill_count))
+        if (n_layers < 0 || (n_layers > 0 && !dst_layers))
+            return fail(KVR_E_ARG, "dst_layers is required to replay fills");
+        for (int32_t t = 0; t < n_layers; ++t)
+            if (int rc = check_layer(ctx, dst_layers[t]))
+                return rc;
+        if (n > 0 && n_layers > 0 && (!fills || !fill_count))
             return fail(KVR_E_ARG, "fills and fill_count are required to replay fills");
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -378,8 +382,9 @@ int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n
         return rc;
     if (n == 0)
         return ok();
-    if (mode == KVR_REUSE_DISTINCT_PAYLOAD) {
-        hipError_t e = kvr::launch_refill(ctx, dst_layer, n, req_ids, fills, fill_count, status, s);
+    if (mode == KVR_REUSE_DISTINCT_PAYLOAD && n_layers > 0) {
+        hipError_t e = kvr::launch_refill(ctx, dst_layers, n_layers, n, req_ids, fills, fill_count,
+                                          status, s);
         if (e != hipSuccess)
             return hip_fail(e, "replay launch");
     }

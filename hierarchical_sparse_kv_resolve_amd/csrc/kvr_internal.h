@@ -64,9 +64,11 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
 size_t resolve_lds_bytes(const Shape &sh);
 hipError_t prepare_resolve_kernel();
 
-hipError_t launch_refill(const kvr_ctx *c, int32_t layer, int32_t n, const int32_t *req_ids,
-                         const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
-                         hipStream_t s);
+// Copies the fills of each request from the host store into the hot cache of
+// every listed layer.
+hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_layers, int32_t n,
+                         const int32_t *req_ids, const kvr_fill *fills, const int32_t *fill_count,
+                         int32_t *status, hipStream_t s);
 
 struct GatherTarget {
     int32_t layer;

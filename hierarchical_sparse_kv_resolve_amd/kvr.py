@@ -73,7 +73,7 @@ def lib():
             "kvr_resolve_rows": [P, I, P, P, P, I, P, P, P, I, P, P, P],
             "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
-            "kvr_reuse_locations": [P, I, I, I, P, P, P, P, I, P, P, P, P],
+            "kvr_reuse_locations": [P, I, I, P, I, P, P, P, P, I, P, P, P, P],
             "kvr_status_summary": [P, I, P],
             "kvr_host_alloc": [U, P],
             "kvr_host_free": [P],
@@ -195,9 +195,11 @@ class Context:
         _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),
                                                  _ptr(union_count), _ptr(map_), _stream(stream)))
 
-    def reuse_locations(self, mode, dst_layer, n, req_ids, src_loc, dst_loc, count, stride,
+    def reuse_locations(self, mode, dst_layers, n, req_ids, src_loc, dst_loc, count, stride,
                         fills=None, fill_count=None, status=None, stream=None):
-        _check(lib().kvr_reuse_locations(self.handle, mode, dst_layer, n, _ptr(req_ids),
+        layers = list(dst_layers or [])
+        arr_l = (ctypes.c_int32 * max(1, len(layers)))(*layers)
+        _check(lib().kvr_reuse_locations(self.handle, mode, len(layers), arr_l, n, _ptr(req_ids),
                                          _ptr(src_loc), _ptr(dst_loc), _ptr(count), stride,
                                          _ptr(fills), _ptr(fill_count), _ptr(status),
                                          _stream(stream)))

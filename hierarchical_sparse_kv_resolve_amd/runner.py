@@ -39,7 +39,7 @@ class _NoTimer:
 _NO = _NoTimer()
 
 
-def _no_timer(name):
+def _no_timer(name, stream=None):
     return _NO
 
 
@@ -124,51 +124,116 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, stream=None, timer=None):
-        """Enqueue decode step s (staged beforehand).  No host synchronisation.
+    def step(self, s: int, timer=None, prefetch_groups: int = 0):
+        """Enqueue decode step s (staged beforehand) on the current stream.  No
+        host synchronisation.
 
-        `timer(name)` may return a context manager that brackets a call with
-        events on the stream (used by the benchmark); with a timer the host
-        refill of layer 0 is issued as its own replay call so it can be timed
-        apart from the resolve (the result is the same)."""
+        prefetch_groups = 0: resolve fills payload layer 0 from host, one
+        replay call fills the other layers, one gather call covers them all.
+        prefetch_groups = G > 0 (layers with shared indices and distinct
+        payloads): the host fills of all layers are issued on a side stream in
+        G groups of layers, and each group's gather starts on the current
+        stream as soon as that group's fills are in, so host-link traffic of
+        later groups overlaps the HBM traffic of earlier gathers.
+
+        `timer(name, stream)` may return a context manager that brackets a
+        call with events (used by the benchmark)."""
+        torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
         tm = timer or _no_timer
-        with tm("append"):
-            ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=stream)
+        main = torch.cuda.current_stream()
+        with tm("append", main):
+            ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
         for g in range(cfg.groups):
             sel = self.sel_dev[s][g]
             k = sel.shape[-1]
             if cfg.q > 1:
-                with tm("dedup"):
+                with tm("dedup", main):
                     ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
-                                                self.map, stream=stream)
+                                                self.map, stream=main)
                 src, count, stride = self.union, self.union_count, cfg.q * k
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            fill_layer = -1 if timer else 0
-            with tm("resolve"):
+            pipelined = prefetch_groups > 0 and cfg.reuse == "distinct"
+            fill_layer = -1 if (timer or pipelined) else 0
+            with tm("resolve", main):
                 ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
-                                 self.status[g], self.stats, stream=stream)
-            if timer:
-                with tm("refill"):
-                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, 0, n, None, loc, None, count,
-                                        stride, fills, fc, stream=stream)
-            if cfg.reuse == "distinct":
-                for l in range(1, self.nl):
-                    with tm("replay"):
-                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, l, n, None, loc, None,
-                                            count, stride, fills, fc, stream=stream)
-                with tm("gather"):
-                    ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
-                                    self.outs[g], self.gather_status, stream=stream)
-            else:
-                with tm("gather"):
+                                 self.status[g], self.stats, stream=main)
+            if cfg.reuse != "distinct":
+                if fill_layer < 0:
+                    with tm("refill", main):
+                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
+                                            count, stride, fills, fc, stream=main)
+                with tm("gather", main):
                     ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
-                                    self.gather_status, stream=stream)
+                                    self.gather_status, stream=main)
                 for _ in range(1, cfg.layers_per_group):
-                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, 0, n, None, loc, None, count,
-                                        stride, stream=stream)
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=main)
+            elif not pipelined:
+                layers = list(range(1 if fill_layer == 0 else 0, self.nl))
+                if layers:
+                    with tm("refill", main):
+                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, layers, n, None, loc,
+                                            None, count, stride, fills, fc, stream=main)
+                with tm("gather", main):
+                    ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
+                                    self.outs[g], self.gather_status, stream=main)
+            else:
+                groups = np.array_split(np.arange(self.nl), min(prefetch_groups, self.nl))
+                resolved = torch.cuda.Event()
+                resolved.record(main)
+                side = self._side()
+                side.wait_event(resolved)
+                ready = []
+                for grp in groups:
+                    with tm("refill", side):
+                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, grp.tolist(), n, None,
+                                            loc, None, count, stride, fills, fc, stream=side)
+                    ev = torch.cuda.Event()
+                    ev.record(side)
+                    ready.append(ev)
+                for grp, ev in zip(groups, ready):
+                    main.wait_event(ev)
+                    with tm("gather", main):
+                        ctx.gather_rows(grp.tolist(), n, None, loc, count, stride,
+                                        [self.outs[g][l] for l in grp], self.gather_status,
+                                        stream=main)
+
+    def snapshot(self) -> dict:
+        """Device copies of the mutable state (metadata, hot caches, tails)."""
+        return {"L": self.L.clone(), "tag": self.tag.clone(), "stamp": self.stamp.clone(),
+                "clock": self.clock.clone(), "hot": [h.clone() for h in self.hot],
+                "tail": [t.clone() for t in self.tail], "stats": self.stats.clone()}
+
+    def restore(self, snap: dict) -> None:
+        for name in ("L", "tag", "stamp", "clock", "stats"):
+            getattr(self, name).copy_(snap[name])
+        for dst, src in zip(self.hot, snap["hot"]):
+            dst.copy_(src)
+        for dst, src in zip(self.tail, snap["tail"]):
+            dst.copy_(src)
+
+    def capture(self, steps, prefetch_groups: int = 0):
+        """Capture the launches of `steps` into one HIP graph (nothing runs
+        until it is replayed).  Each replay runs those decode steps again from
+        whatever state the buffers hold."""
+        torch = self.torch
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()  # default priority
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for s in steps:
+                    self.step(s, prefetch_groups=prefetch_groups)
+        torch.cuda.current_stream().wait_stream(cap)
+        return graph
+
+    def _side(self):
+        if getattr(self, "_side_stream", None) is None:
+            self._side_stream = self.torch.cuda.Stream()  # default priority
+        return self._side_stream
 
     # ------------------------------------------------------------------ read-back (syncs)
     def state(self) -> dict:

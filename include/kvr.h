@@ -77,8 +77,9 @@ typedef enum kvr_reuse_mode {
      * as is (dst_loc NULL = alias, zero bytes moved; else a copy of it). */
     KVR_REUSE_SHARED_SOURCE = 0,
     /* Shared indices, distinct per-layer payloads: the rows filled from host
-     * for one layer are fetched into the same hot slots of dst_layer from
-     * dst_layer's host store; dst_loc (optional) receives a copy of src_loc. */
+     * for one layer are fetched into the same hot slots of every destination
+     * layer from that layer's host store; dst_loc (optional) receives a copy
+     * of src_loc. */
     KVR_REUSE_DISTINCT_PAYLOAD = 1,
 } kvr_reuse_mode;
 
@@ -165,7 +166,7 @@ int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void 
  *   fills     (device) kvr_fill [n][B] out: the rows copied from host, by
  *             ascending row; fill_count (device) int32 [n] out
  *   fill_layer payload layer refilled from host now, or -1 for none (the
- *             fills can be replayed per layer with kvr_reuse_locations)
+ *             fills can be replayed into any layers with kvr_reuse_locations)
  *   status    (device) int32 [n] out, required
  *   stats     (device) kvr_stats or NULL, added to
  * Per request, with now = clock + 1 (one tick per call):
@@ -206,14 +207,20 @@ int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, c
                                 void *stream);
 
 /* Location reuse across layers ("Model-specific reuse"); see kvr_reuse_mode.
+ *   SHARED_SOURCE: dst_layers may be NULL; dst_loc (optional) gets src_loc.
+ *   DISTINCT_PAYLOAD: the fills are replayed into every listed layer, all in
+ *     one launch per 24 layers: row `row` of that layer's host store is copied
+ *     into hot slot `slot` of that layer.
+ *   dst_layers (host) int32 [n_layers]
  *   src_loc/dst_loc (device) uint32 [n][stride]; count (device) int32 [n] or NULL
  *   fills/fill_count (device): from the resolve call (DISTINCT_PAYLOAD only)
  *   status (device) int32 [n] or NULL: set to KVR_E_RANGE if a fill names a
  *   row or slot out of range, otherwise not written. */
-int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t dst_layer, int32_t n,
-                        const int32_t *req_ids, const uint32_t *src_loc, uint32_t *dst_loc,
-                        const int32_t *count, int32_t stride, const kvr_fill *fills,
-                        const int32_t *fill_count, int32_t *status, void *stream);
+int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *dst_layers,
+                        int32_t n, const int32_t *req_ids, const uint32_t *src_loc,
+                        uint32_t *dst_loc, const int32_t *count, int32_t stride,
+                        const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
+                        void *stream);
 
 /* Host helper, after the caller has synchronised and copied status to host:
  * number of failed requests; *first_bad = index of the first (or -1). */

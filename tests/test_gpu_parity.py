@@ -57,7 +57,7 @@ def _compare_state(gpu, run, reqs):
     assert np.array_equal(st["stamp"][idx], src.stamp)
 
 
-def _run_parity(cfg, reqs=None, check_hot=True, max_new=None):
+def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0):
     inputs = Inputs(cfg, max_new=max_new)
     reqs = list(range(cfg.n_req)) if reqs is None else list(reqs)
     pool = []
@@ -75,7 +75,7 @@ def _run_parity(cfg, reqs=None, check_hot=True, max_new=None):
             o = run.step(s, sels=[x[reqs] for x in sels])
             # groups of one step share buffers per group, so run the GPU step and
             # read every group back afterwards
-            gpu.step(s)
+            gpu.step(s, prefetch_groups=prefetch_groups)
             st = gpu.state()
             assert (st["L"] == inputs.length_at(s)).all()
             assert (gpu.append_status.cpu().numpy() == 0).all()
@@ -94,6 +94,10 @@ def _run_parity(cfg, reqs=None, check_hot=True, max_new=None):
         if reqs == list(range(cfg.n_req)):
             gs = gpu.stats_dict()
             os_ = dict(zip(orc.STAT_NAMES, (int(x) for x in run.src.stats)))
+            if prefetch_groups:
+                # the resolve call copies nothing itself here: its replays do
+                assert gs.pop("host_bytes") == 0
+                os_.pop("host_bytes")
             assert gs == os_, (gs, os_)
         print(f"[parity] {cfg.name}: ok", flush=True)
     finally:
@@ -108,6 +112,16 @@ def test_reduced_workload_parity(c):
 @pytest.mark.parametrize("c", [1, 2, 3, 4])
 def test_full_workload_parity(c):
     _run_parity(FULL[c])
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 8])
+def test_prefetch_pipeline_parity(groups):
+    """Host fills on a side stream in layer groups, gathers as groups complete:
+    the schedule the benchmark times, same results as the one-stream schedule."""
+    _run_parity(tiny(2), prefetch_groups=groups)
+    _run_parity(tiny(4), prefetch_groups=groups)
+    if groups == 2:
+        _run_parity(FULL[2], prefetch_groups=groups)
 
 
 def test_full_long_context_parity_sampled():
@@ -307,5 +321,46 @@ def test_closed_form_bytes_full_glm_shape():
                 for l in range(cfg.payload_layers):
                     exp = payload_np(l, r, sel[r, js], cfg.R, cfg.seed)
                     assert np.array_equal(rec["out"][l][r, js], exp)
+    finally:
+        gpu.close()
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+
+@pytest.mark.parametrize("prefetch_groups", [0, 2])
+def test_graph_replays_match_oracle(prefetch_groups):
+    """Decode steps captured into HIP graphs give the oracle's results: a
+    multi-step graph replayed once, then a one-step graph replayed three times
+    (each replay is another decode step on the evolving state), with eager
+    read-backs and synchronisation between replays."""
+    import torch
+    cfg = tiny(2).with_(steps=8)
+    inputs = Inputs(cfg)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    try:
+        gpu.stage(range(cfg.steps))
+        gpu.step(0, prefetch_groups=prefetch_groups)
+        o = run.step(0)
+        _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
+        g = gpu.capture(range(1, 4), prefetch_groups=prefetch_groups)
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(1, 4):
+            o = run.step(s)
+        _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
+        _compare_state(gpu, run, reqs)
+        one = gpu.capture([4], prefetch_groups=prefetch_groups)
+        for rep in range(3):
+            one.replay()
+            torch.cuda.synchronize()
+            o = run.step(4)  # the same inputs again: one more row, same selection
+            _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
+            _compare_state(gpu, run, reqs)
+            assert (gpu.gather_status.cpu().numpy() == 0).all()
+        for l in range(cfg.payload_layers):
+            assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l])
     finally:
         gpu.close()
