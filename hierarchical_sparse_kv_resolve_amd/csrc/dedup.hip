@@ -4,9 +4,10 @@
 // their selections are merged into one ascending union that is resolved
 // once, plus a map from every query entry to its union index.
 //
-// One 1024-thread workgroup per request: the q*k entries are sorted in LDS
-// (bitonic), duplicates are dropped with a workgroup scan, and each entry
-// finds its union index by binary search in LDS.
+// One 1024-thread workgroup per request: the q*k entries are sorted with the
+// register/shuffle bitonic network (LDS only for strides 64..512), duplicates
+// are dropped with a workgroup scan, and each entry finds its union index by
+// binary search in LDS, several searches per thread interleaved.
 #include <climits>
 
 #include "block.h"
@@ -28,12 +29,12 @@ __global__ __launch_bounds__(NT) void dedup_kernel(int32_t q, int32_t k, const i
     __shared__ int sScan[NW];
     const int i = blockIdx.x;
     const int n_all = q * k;
-    const int np2 = next_pow2(n_all > 0 ? n_all : 1);
     const int32_t *in = sel + (int64_t)i * n_all;
-    for (int t = threadIdx.x; t < np2; t += NT)
-        s[t] = t < n_all ? in[t] : INT_MAX;
+    for (int t = threadIdx.x; t < n_all; t += NT)
+        s[t] = in[t];
     __syncthreads();
-    bitonic_sort<NT>(s, np2);
+    if (n_all > 0)
+        block_sort_lds<NT, int32_t>(s, n_all, INT_MAX);
 
     const int per = (n_all + NT - 1) / NT;
     const int beg = threadIdx.x * per;
@@ -65,8 +66,23 @@ __global__ __launch_bounds__(NT) void dedup_kernel(int32_t q, int32_t k, const i
     if (threadIdx.x == 0)
         union_count[i] = u;
     int32_t *mout = map + (int64_t)i * n_all;
-    for (int t = threadIdx.x; t < n_all; t += NT)
-        mout[t] = lds_find(s, u, in[t]);
+    // eight interleaved searches per round
+    for (int base = 0; base < n_all; base += 8 * NT) {
+        int32_t key[8];
+        int idx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = base + e * NT + threadIdx.x;
+            key[e] = t < n_all ? in[t] : INT_MIN;
+        }
+        lds_find_many<8>(s, u, key, idx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = base + e * NT + threadIdx.x;
+            if (t < n_all)
+                mout[t] = idx[e];
+        }
+    }
 }
 
 }  // namespace
@@ -80,7 +96,9 @@ hipError_t prepare_dedup_kernel()
 hipError_t launch_dedup(int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
                         int32_t *union_count, int32_t *map, hipStream_t s)
 {
-    const size_t lds = (size_t)next_pow2(q * k > 0 ? q * k : 1) * 4;
+    // the sort works on max(NT, next power of two >= q*k) entries
+    const int n_all = q * k;
+    const size_t lds = (size_t)next_pow2(n_all > NT ? n_all : NT) * 4;
     hipLaunchKernelGGL(dedup_kernel, dim3(n), dim3(NT), lds, s, q, k, sel, union_rows, union_count,
                        map);
     return hipGetLastError();

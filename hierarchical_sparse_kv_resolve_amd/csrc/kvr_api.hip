@@ -130,6 +130,11 @@ int kvr_create(const kvr_config *cfg, kvr_ctx **out)
     sh.pool_rows = c.pool_pages * c.page_rows;
     sh.host_rows = (int64_t)c.history_rows + c.max_new_rows;
     ctx->resolve_lds = kvr::resolve_lds_bytes(sh);
+    if (ctx->resolve_lds == 0) {
+        delete ctx;
+        return fail(KVR_E_ARG, "hot_slots %d with sel_cap %d does not fit one workgroup's LDS",
+                    c.hot_slots, c.sel_cap);
+    }
 
     hipError_t e = hipGetDevice(&ctx->device);
     if (e != hipSuccess) {

@@ -10,7 +10,7 @@ namespace kvr {
 
 constexpr int kMaxHotSlots = 8192;
 constexpr int kMaxSelCap = 8192;
-constexpr int kMaxUnion = 16384;       // q * k of one verification block
+constexpr int kMaxUnion = 8192;        // q * k of one verification block
 constexpr int kGatherLayersPerLaunch = 24;
 
 // Location word layout (bits 31..30 place, 29..0 index).

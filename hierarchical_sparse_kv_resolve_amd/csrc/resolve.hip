@@ -10,19 +10,25 @@
 // One workgroup of 1024 threads (16 waves) owns one request for the whole
 // call, so every decision about that request's hot cache is made in one place
 // and LDS holds all of it:
-//   sU    the distinct pending rows, ascending (wave-ballot compaction, a
-//         register/shuffle bitonic sort, workgroup-scan dedup),
-//   sSlot per pending row: its hot slot, or the rank of the miss,
-//   sKey  the victims' (stamp << 32 | slot) keys in victim order.
-// The hot-cache scan touches each of the B tags exactly once (a binary search
-// of the tag among the sorted pending rows), so the work per call is bounded
-// by B and by the selection size, never by the history length.
+//   hkey/hval  an open-addressing hash of the distinct pending rows (insert
+//              if absent dedups them; each thread keeps the entries of its
+//              selection entries in registers); hval holds the row's hot
+//              slot, the rank of the miss, or the filled slot,
+//   sKey       the misses in ascending row order and then the victims'
+//              (stamp << 32 | slot) keys in victim order.
+// The hot-cache scan looks each of the B tags up once in the hash, so the
+// work per call is bounded by B and by the selection size, never by the
+// history length.  Tags and stamps are loaded at kernel start so their
+// latency hides behind step 1.
 //
 // Victims are the m smallest (stamp, slot) keys among the slots not hit in the
-// call.  Instead of sorting all B keys, a radix select over stamp digits finds
-// the threshold stamp tau; every candidate older than tau is a victim, and the
-// youngest victims are the first candidates stamped tau in slot order.  Only
-// the candidates older than tau are sorted, and only when their stamps differ.
+// call.  A radix select over stamp digits finds the threshold stamp tau;
+// every candidate older than tau is a victim, and the youngest victims are
+// the first candidates stamped tau in slot order (ordered compaction with
+// wave ballots).  Only the candidates older than tau are sorted, and only
+// when their stamps differ.  Misses take victims in ascending row order.
+// Up to 1024 keys are put in order by counting (one broadcast pass over LDS),
+// more by the register/shuffle bitonic network.
 #include <climits>
 
 #include "block.h"
@@ -33,11 +39,17 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int NW = NT / kWave;
-constexpr int EK = kMaxSelCap / NT;    // selection entries per thread
-constexpr int EB = kMaxHotSlots / NT;  // hot slots per thread
+// Selection entries (EK) and hot slots (EB) per thread are template
+// parameters: the launch picks the smallest of 1, 2, 4, 8 that covers sel_cap
+// and B, so small shapes keep fewer live registers.
+constexpr int kCntE = 8;  // hot-slot entries per thread the compaction counters cover
+constexpr int32_t kEmpty = -1;
 constexpr int32_t kNoSlot = INT_MAX;
 constexpr int32_t kFilledBit = 1 << 30;
-constexpr uint32_t kPending = 0xFFFFFFFEu;  // not a valid location word
+// A pending entry keeps its hash entry in its location word until the end:
+// place bits 3 with an index below 2^30 is no valid word (invalid is all ones).
+constexpr uint32_t kPendingTag = 3u << 30;
+__device__ __forceinline__ bool is_pending(uint32_t w) { return (w >> 30) == 3u && w != 0xFFFFFFFFu; }
 
 struct ResolveArgs {
     Shape sh;
@@ -57,9 +69,102 @@ struct ResolveArgs {
     int32_t *fill_count;
     int32_t *status;
     kvr_stats *stats;
-    int32_t u_cap;  // LDS entries of sU and sSlot: max(NT, next_pow2(sel_cap))
-    int32_t b_cap;  // LDS entries of sKey: max(NT, next_pow2(B))
+    int32_t vc;  // sKey entries: max(NT, next_pow2(min(B, sel_cap)))
+    int32_t hs;  // hash entries
 };
+
+__device__ __forceinline__ int hslot(int32_t key, int hs)
+{
+    return (int)(((uint64_t)((uint32_t)key * 0x9E3779B1u) * (uint32_t)hs) >> 32);
+}
+
+__device__ __forceinline__ int hnext(int idx, int hs) { return idx + 1 == hs ? 0 : idx + 1; }
+
+// Insert key (>= 0) if absent.  Returns the key's entry; `fresh` tells
+// whether this call put it there.  The table always keeps an empty entry
+// (more entries than keys), so probing ends.
+__device__ __forceinline__ int hinsert(int32_t *hkey, int hs, int32_t key, bool &fresh)
+{
+    int idx = hslot(key, hs);
+    while (true) {
+        const int32_t old = atomicCAS(&hkey[idx], kEmpty, key);
+        if (old == kEmpty || old == key) {
+            fresh = old == kEmpty;
+            return idx;
+        }
+        idx = hnext(idx, hs);
+    }
+}
+
+// Ascending order of n <= NT distinct keys s[0..n) in place, by counting for
+// each key the keys below it (no sorting network).  P = NT / next_pow2(n)
+// consecutive lanes share one key and split the count, so each thread reads
+// about n * n / NT keys; the partial counts meet through shuffles.  Every
+// thread of the workgroup must call it.
+template <int NT, typename K>
+__device__ __forceinline__ void rank_sort_small(K *s, int n)
+{
+    const int tid = threadIdx.x;
+    int P = NT / next_pow2(n > 0 ? n : 1);
+    P = P > kWave ? kWave : P;
+    const int el = tid / P, part = tid % P;
+    const K mine = el < n ? s[el] : K(0);
+    int below = 0;
+    for (int j = part; j < n; j += P)
+        below += s[j] < mine ? 1 : 0;
+    for (int d = 1; d < P; d <<= 1)
+        below += __shfl_xor(below, d, kWave);
+    __syncthreads();
+    if (el < n && part == 0)
+        s[below] = mine;
+    __syncthreads();
+}
+
+// Ascending order of s[0..n) of distinct keys: counting for small n, the
+// bitonic network otherwise.
+template <int NT, typename K>
+__device__ __forceinline__ void order_keys(K *s, int n, K pad)
+{
+    if (n <= NT)
+        rank_sort_small<NT, K>(s, n);
+    else
+        block_sort_lds<NT, K>(s, n, pad);
+}
+
+// E lookups with interleaved probes: idx[e] = entry of key[e], or -1 when it
+// is absent or key[e] < 0.
+template <int E>
+__device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const int32_t (&key)[E],
+                                           int (&idx)[E])
+{
+    int cur[E];
+    bool live[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        live[e] = key[e] >= 0;
+        cur[e] = live[e] ? hslot(key[e], hs) : 0;
+        idx[e] = -1;
+    }
+    bool any = true;
+    while (any) {
+        any = false;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (live[e]) {
+                const int32_t kk = hkey[cur[e]];
+                if (kk == key[e]) {
+                    idx[e] = cur[e];
+                    live[e] = false;
+                } else if (kk == kEmpty) {
+                    live[e] = false;
+                } else {
+                    cur[e] = hnext(cur[e], hs);
+                    any = true;
+                }
+            }
+        }
+    }
+}
 
 __device__ __forceinline__ void fail_request(const ResolveArgs &a, int i, int k, int code)
 {
@@ -76,28 +181,28 @@ __device__ __forceinline__ void fail_request(const ResolveArgs &a, int i, int k,
     }
 }
 
-// Digit of `rel` at bit `shift` (8-bit digits).
-__device__ __forceinline__ int digit8(uint32_t rel, int shift) { return (rel >> shift) & 0xFF; }
-
+template <int EK, int EB>
 __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
 {
+    static_assert(EB <= kCntE && 2 * kCntE * NW == 4 * kWave, "compaction counter layout");
     extern __shared__ __align__(16) uint8_t lds[];
     uint64_t *sKey = reinterpret_cast<uint64_t *>(lds);
-    int32_t *sU = reinterpret_cast<int32_t *>(sKey + a.b_cap);
-    int32_t *sSlot = sU + a.u_cap;
-    __shared__ int sScan[NW];
-    __shared__ unsigned long long sScan64[NW];
-    __shared__ unsigned long long sRed[NW];
-    __shared__ uint32_t sRedU[2 * NW];
+    int32_t *hkey = reinterpret_cast<int32_t *>(sKey + a.vc);
+    int32_t *hval = hkey + a.hs;
     __shared__ int sHist[256];
+    __shared__ int sCnt[2 * kCntE * NW];  // [kind][e][wave]; e >= EB stays 0
+    __shared__ uint32_t sRedU[2 * NW];
     __shared__ int sPick[2];
-    __shared__ int sPend;
+    __shared__ int sUnique;
+    __shared__ int sMiss;
     __shared__ int sRangeErr;
     __shared__ int sHostErr;
+    __shared__ int sTagSink;
 
     const Shape &sh = a.sh;
     const int i = blockIdx.x;
     const int tid = threadIdx.x;
+    const int hs = a.hs;
     const int r = a.req_ids ? a.req_ids[i] : i;
     int k = a.sel_count ? a.sel_count[i] : a.stride;
     if (r < 0 || r >= sh.n_req || k < 0 || k > a.stride) {
@@ -106,16 +211,35 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     }
     const int32_t *sel = a.sel + (int64_t)i * a.stride;
     uint32_t *loc = a.loc + (int64_t)i * a.stride;
+    int32_t *tag = a.tag + (int64_t)r * sh.B;
+    uint32_t *stamp = a.stamp + (int64_t)r * sh.B;
+
+    // Tags and stamps of this thread's slots (slot b = e*NT + tid), issued first.
+    int32_t t[EB];
+    uint32_t st[EB];
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+        const int b = e * NT + tid;
+        t[e] = b < sh.B ? tag[b] : -1;
+        st[e] = b < sh.B ? stamp[b] : 0u;
+    }
     const int32_t L = a.L[r];
     const uint32_t clk = a.clock[r];
     const int32_t tail_lo = sh.T > 0 ? max(L - sh.T, 0) : L;
     const int32_t *pmap = a.page_map + (int64_t)r * sh.n_pages;
     const uint8_t *hvalid = a.host_valid + (int64_t)r * sh.n_pages;
-    int32_t *tag = a.tag + (int64_t)r * sh.B;
-    uint32_t *stamp = a.stamp + (int64_t)r * sh.B;
 
+    for (int x = tid; x < hs; x += NT) {
+        hkey[x] = kEmpty;
+        hval[x] = kNoSlot;
+    }
+    for (int x = tid; x < 256; x += NT)
+        sHist[x] = 0;
+    for (int x = tid; x < 2 * kCntE * NW; x += NT)
+        sCnt[x] = 0;
     if (tid == 0) {
-        sPend = 0;
+        sUnique = 0;
+        sMiss = 0;
         sRangeErr = 0;
         sHostErr = 0;
     }
@@ -123,24 +247,18 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
 
     // Step 1 and range check.  Entry e of this thread is selection j = e*NT+tid;
     // its row and location word stay in registers until the end.  Rows in the
-    // tail window or in a ready complete page are found here; the others are
-    // compacted into sU by wave ballots.
-    int32_t pos[EK];
+    // tail window or in a ready complete page are found here; the others go
+    // into the hash once each.
     uint32_t word[EK];
+    int owned = 0, nohost = 0, fresh_n = 0;
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        pos[e] = -1;
+    for (int e = 0; e < EK; ++e)
         word[e] = 0;
-    }
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
         const int j = e * NT + tid;
-        if (e * NT >= k)
-            break;  // uniform: no entry of this round exists
-        bool pending = false;
         if (j < k) {
             const int32_t p = sel[j];
-            pos[e] = p;
             if (p < 0 || p >= L) {
                 sRangeErr = 1;
             } else if (p >= tail_lo) {
@@ -150,18 +268,41 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
                 if (phys >= 0) {
                     word[e] = (1u << kPlaceShift) | (uint32_t)((int64_t)phys * sh.P + p % sh.P);
                 } else {
-                    word[e] = kPending;
-                    pending = true;
+                    bool fresh;
+                    word[e] = kPendingTag | (uint32_t)hinsert(hkey, hs, p, fresh);
+                    if (fresh) {
+                        owned |= 1 << e;
+                        ++fresh_n;
+                        if (p < sh.H && !hvalid[p / sh.P])
+                            nohost |= 1 << e;
+                    }
                 }
             }
         }
-        const uint64_t m = __ballot(pending);
-        int wbase = 0;
-        if (lane_id() == 0 && m)
-            wbase = atomicAdd(&sPend, __popcll(m));
-        wbase = __shfl(wbase, 0, kWave);
-        if (pending)
-            sU[wbase + ballot_rank(m)] = pos[e];
+    }
+    {
+        const int wf = wave_sum(fresh_n);
+        uint32_t lo = 0xFFFFFFFFu, hi = 0;
+        int32_t tmax = -1;
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            if (e * NT + tid < sh.B) {
+                lo = st[e] < lo ? st[e] : lo;
+                hi = st[e] > hi ? st[e] : hi;
+            }
+            tmax = t[e] > tmax ? t[e] : tmax;  // waits for the tags here, in step 1's shadow
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        tmax = wave_max(tmax);
+        if (lane_id() == 0) {
+            if (wf)
+                atomicAdd(&sUnique, wf);
+            sRedU[wave_id()] = lo;
+            sRedU[NW + wave_id()] = hi;
+            if (wave_id() == 0)
+                sTagSink = tmax;
+        }
     }
     __syncthreads();
     if (sRangeErr) {
@@ -172,163 +313,103 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         fail_request(a, i, k, KVR_E_STATE);
         return;
     }
-    const uint32_t now = clk + 1;
-    const int n_pend = sPend;
-
-    // Distinct pending rows, ascending.
-    int nU = 0;
-    if (n_pend > 0) {
-        block_sort_lds<NT, int32_t>(sU, n_pend, INT_MAX);
-        const int per = (n_pend + NT - 1) / NT;
-        const int beg = tid * per;
-        int32_t v[EK];
-        int keep = 0, cnt = 0;
-#pragma unroll
-        for (int e = 0; e < EK; ++e) {
-            const int idx = beg + e;
-            if (e < per && idx < n_pend) {
-                v[e] = sU[idx];
-                if (idx == 0 || sU[idx - 1] != v[e]) {
-                    keep |= 1 << e;
-                    ++cnt;
-                }
-            }
-        }
-        int off = block_exclusive_scan<NT>(cnt, sScan, nU);
-#pragma unroll
-        for (int e = 0; e < EK; ++e)
-            if (keep & (1 << e))
-                sU[off++] = v[e];
-        for (int t = tid; t < nU; t += NT)
-            sSlot[t] = kNoSlot;
-        __syncthreads();
-    }
-
-    // Step 2: each of the B tags is looked up once among the pending rows
-    // (EB searches per thread run interleaved).  If two slots ever held one
-    // row, the lower slot is the hit.
-    int fidx[EB];
-    uint32_t st[EB];
-    {
-        int32_t t[EB];
-#pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            const int b = e * NT + tid;
-            t[e] = (b < sh.B) ? tag[b] : -1;
-            st[e] = 0;
-        }
-        if (nU > 0) {
-            lds_find_many<EB>(sU, nU, t, fidx);
-#pragma unroll
-            for (int e = 0; e < EB; ++e) {
-                if (t[e] < 0)
-                    fidx[e] = -1;
-                if (fidx[e] >= 0)
-                    atomicMin(&sSlot[fidx[e]], e * NT + tid);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < EB; ++e)
-                fidx[e] = -1;
-        }
-    }
-    __syncthreads();
-
-    // Misses: rank them in ascending row order; check host copies.
-    int m_total = 0;
-    if (nU > 0) {
-        const int per = (nU + NT - 1) / NT;
-        const int beg = tid * per;
-        int cnt = 0;
-        for (int e = 0; e < per; ++e) {
-            const int idx = beg + e;
-            if (idx < nU && sSlot[idx] == kNoSlot) {
-                ++cnt;
-                const int32_t u = sU[idx];
-                if (u < sh.H && !hvalid[u / sh.P])
-                    sHostErr = 1;
-            }
-        }
-        int off = block_exclusive_scan<NT>(cnt, sScan, m_total);
-        for (int e = 0; e < per; ++e) {
-            const int idx = beg + e;
-            if (idx < nU && sSlot[idx] == kNoSlot)
-                sSlot[idx] = -1 - off++;  // miss rank, negative
-        }
-        __syncthreads();
-    }
+    const int nU = sUnique;
     if (nU > sh.B) {
         fail_request(a, i, k, KVR_E_CAPACITY);
         return;
     }
+    const uint32_t now = clk + 1;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = sRedU[w] < lo ? sRedU[w] : lo;
+        hi = sRedU[NW + w] > hi ? sRedU[NW + w] : hi;
+    }
+
+    // Step 2: every tag is looked up once among the pending rows.  If two
+    // slots ever held one row, the lower slot is the hit.
+    int fidx[EB];
+    hfind_many<EB>(hkey, hs, t, fidx);
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+        if (fidx[e] >= 0)
+            atomicMin(&hval[fidx[e]], e * NT + tid);
+    __syncthreads();
+
+    // Misses: pending rows no slot holds (each checked once, by the entry that
+    // inserted it); each needs a host copy.  The list packs (row, hash entry).
+    uint64_t *sMissList = sKey;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        bool miss = false;
+        const uint32_t h = word[e] & kIndexMask;
+        if ((owned >> e) & 1) {
+            miss = hval[h] == kNoSlot;
+            if (miss && ((nohost >> e) & 1))
+                sHostErr = 1;
+        }
+        const uint64_t mb = __ballot(miss);
+        int wbase = 0;
+        if (lane_id() == 0 && mb)
+            wbase = atomicAdd(&sMiss, __popcll(mb));
+        wbase = __shfl(wbase, 0, kWave);
+        if (miss)
+            sMissList[wbase + ballot_rank(mb)] = ((uint64_t)(uint32_t)hkey[h] << 32) | h;
+    }
+    __syncthreads();
     if (sHostErr) {
         fail_request(a, i, k, KVR_E_NO_HOST_COPY);
         return;
     }
+    const int m_total = sMiss;
 
-    // Step 3: victims = the m_total smallest (stamp, slot) among slots not hit.
     if (m_total > 0) {
+        // Misses in ascending row order; each learns its rank.
+        order_keys<NT, uint64_t>(sMissList, m_total, ~0ull);
+        for (int q = tid; q < m_total; q += NT)
+            hval[(uint32_t)sMissList[q]] = -1 - q;
+        __syncthreads();
+
+        // Step 3: victims = the m_total smallest (stamp, slot) among the slots
+        // whose tag is not a hit of this call.
         bool cand[EB];
-        uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
         for (int e = 0; e < EB; ++e) {
             const int b = e * NT + tid;
-            cand[e] = b < sh.B && !(fidx[e] >= 0 && sSlot[fidx[e]] == b);
-            if (cand[e]) {
-                st[e] = stamp[b];
-                lo = st[e] < lo ? st[e] : lo;
-                hi = st[e] > hi ? st[e] : hi;
-            }
+            cand[e] = b < sh.B && !(fidx[e] >= 0 && hval[fidx[e]] == b);
         }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        if (lane_id() == 0) {
-            sRedU[wave_id()] = lo;
-            sRedU[NW + wave_id()] = hi;
-        }
-        __syncthreads();
-        lo = 0xFFFFFFFFu;
-        hi = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            lo = sRedU[w] < lo ? sRedU[w] : lo;
-            hi = sRedU[NW + w] > hi ? sRedU[NW + w] : hi;
-        }
-        // Radix select of the threshold stamp over rel = stamp - lo, 8 bits at
-        // a time from the highest digit that varies.
+        // Radix select of the threshold stamp over rel = stamp - lo, 8 bits
+        // at a time from the highest digit that varies.
         const uint32_t span = hi - lo;
         int top = 0;
-        while (top < 32 && (span >> top) > 0xFF)
+        while (top < 24 && (span >> top) > 0xFF)
             top += 8;
-        uint32_t prefix = 0;      // digits chosen so far (above `shift + 8`)
-        int m_rem = m_total;      // victims still to take at or above the prefix
-        int c_lt = 0;             // candidates strictly older than the prefix bucket
+        uint32_t prefix = 0;
+        int m_rem = m_total;
+        int c_lt = 0;
         if (span > 0) {
             for (int shift = top; shift >= 0; shift -= 8) {
-                for (int t = tid; t < 256; t += NT)
-                    sHist[t] = 0;
-                __syncthreads();
                 const uint32_t hmask = (shift + 8 >= 32) ? 0u : (0xFFFFFFFFu << (shift + 8));
 #pragma unroll
                 for (int e = 0; e < EB; ++e) {
                     if (cand[e]) {
                         const uint32_t rel = st[e] - lo;
                         if ((rel & hmask) == prefix)
-                            atomicAdd(&sHist[digit8(rel, shift)], 1);
+                            atomicAdd(&sHist[(rel >> shift) & 0xFF], 1);
                     }
                 }
                 __syncthreads();
                 if (wave_id() == 0) {
-                    // lane l holds bins 4l .. 4l+3
+                    // lane l holds bins 4l .. 4l+3; they are cleared for the next pass
                     int c[4], sum = 0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         c[q] = sHist[lane_id() * 4 + q];
+                        sHist[lane_id() * 4 + q] = 0;
                         sum += c[q];
                     }
                     const int incl = wave_inclusive_scan(sum);
                     int below = incl - sum;
-                    // the bin where the running count first reaches m_rem
                     int pick = -1, pick_below = 0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -339,11 +420,11 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
                         below += c[q];
                     }
                     const uint64_t found = __ballot(pick >= 0);
-                    const int src = __ffsll((unsigned long long)found) - 1;
+                    const int src = found ? __ffsll((unsigned long long)found) - 1 : 0;
                     pick = __shfl(pick, src, kWave);
                     pick_below = __shfl(pick_below, src, kWave);
                     if (lane_id() == 0) {
-                        sPick[0] = pick;
+                        sPick[0] = pick < 0 ? 0 : pick;
                         sPick[1] = pick_below;
                     }
                 }
@@ -351,93 +432,94 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
                 prefix |= (uint32_t)sPick[0] << shift;
                 m_rem -= sPick[1];
                 c_lt += sPick[1];
-                __syncthreads();
             }
         }
         const uint32_t tau = lo + prefix;
 
-        // Ordered compaction in slot order: candidates older than tau become
-        // sKey[0 .. c_lt) (then sorted), the first m_rem candidates stamped
-        // tau fill sKey[c_lt .. m_total).  Slot b = e*NT + tid, so the order
-        // is (e, tid); 16-bit fields pack the per-e counts of one thread.
-        uint64_t lt_bits = 0, eq_bits = 0;
+        // Ordered compaction in slot order (b = e*NT + tid, i.e. (e, wave,
+        // lane)): wave ballots give the order inside a wave, one wave scans
+        // the per-(e, wave) counts.  Candidates older than tau go to
+        // sKey[0 .. c_lt), the first m_rem stamped tau to sKey[c_lt ..).
+        uint64_t blt[EB], beq[EB];
+        uint32_t l2 = 0xFFFFFFFFu, h2 = 0;
 #pragma unroll
         for (int e = 0; e < EB; ++e) {
-            if (cand[e]) {
-                if (st[e] < tau)
-                    lt_bits |= 1ull << (8 * e);
-                else if (st[e] == tau)
-                    eq_bits |= 1ull << (8 * e);
+            const bool lt = cand[e] && st[e] < tau;
+            const bool eq = cand[e] && st[e] == tau;
+            blt[e] = __ballot(lt);
+            beq[e] = __ballot(eq);
+            if (lt) {
+                l2 = st[e] < l2 ? st[e] : l2;
+                h2 = st[e] > h2 ? st[e] : h2;
             }
-        }
-        // one scan of 8 byte-wide fields per kind would overflow (counts reach
-        // NT), so scan 4 fields of 16 bits twice per kind
-        int lt_rank[EB], eq_rank[EB];
-        int lt_tot_before = 0, eq_tot_before = 0;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            uint64_t pl = 0, pe = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int e = half * 4 + q;
-                pl |= (uint64_t)((lt_bits >> (8 * e)) & 1) << (16 * q);
-                pe |= (uint64_t)((eq_bits >> (8 * e)) & 1) << (16 * q);
-            }
-            u64 tl, te;
-            const u64 xl = block_exclusive_scan64<NT>(pl, sScan64, tl);
-            const u64 xe = block_exclusive_scan64<NT>(pe, sScan64, te);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int e = half * 4 + q;
-                lt_rank[e] = lt_tot_before + (int)((xl >> (16 * q)) & 0xFFFF);
-                eq_rank[e] = eq_tot_before + (int)((xe >> (16 * q)) & 0xFFFF);
-                lt_tot_before += (int)((tl >> (16 * q)) & 0xFFFF);
-                eq_tot_before += (int)((te >> (16 * q)) & 0xFFFF);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < EB; ++e)
-            if ((lt_bits >> (8 * e)) & 1)
-                sKey[lt_rank[e]] = ((uint64_t)st[e] << 32) | (uint32_t)(e * NT + tid);
-        __syncthreads();
-        if (c_lt > 1) {
-            // sort only when the older candidates carry different stamps
-            uint32_t l2 = 0xFFFFFFFFu, h2 = 0;
-            for (int t = tid; t < c_lt; t += NT) {
-                const uint32_t sv = (uint32_t)(sKey[t] >> 32);
-                l2 = sv < l2 ? sv : l2;
-                h2 = sv > h2 ? sv : h2;
-            }
-            l2 = wave_min(l2);
-            h2 = wave_max(h2);
             if (lane_id() == 0) {
-                sRedU[wave_id()] = l2;
-                sRedU[NW + wave_id()] = h2;
+                sCnt[e * NW + wave_id()] = __popcll(blt[e]);
+                sCnt[kCntE * NW + e * NW + wave_id()] = __popcll(beq[e]);
             }
-            __syncthreads();
-            uint32_t gl = 0xFFFFFFFFu, gh = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                gl = sRedU[w] < gl ? sRedU[w] : gl;
-                gh = sRedU[NW + w] > gh ? sRedU[NW + w] : gh;
-            }
-            __syncthreads();
-            if (gl != gh)  // uniform
-                block_sort_lds<NT, uint64_t>(sKey, c_lt, ~0ull);
         }
-        // the sort above uses sKey as its exchange buffer, so the youngest
-        // victims are placed after it
+        l2 = wave_min(l2);
+        h2 = wave_max(h2);
+        if (lane_id() == 0) {
+            sRedU[wave_id()] = l2;
+            sRedU[NW + wave_id()] = h2;
+        }
+        __syncthreads();
+        if (wave_id() == 0) {
+            // 2 * kCntE * NW = 256 counts, 4 per lane; lanes 0..31 hold the
+            // older kind, lanes 32..63 the tau kind, each scanned on its own
+            int c[4], sum = 0;
 #pragma unroll
-        for (int e = 0; e < EB; ++e)
-            if (((eq_bits >> (8 * e)) & 1) && eq_rank[e] < m_rem)
-                sKey[c_lt + eq_rank[e]] = ((uint64_t)st[e] << 32) | (uint32_t)(e * NT + tid);
+            for (int q = 0; q < 4; ++q) {
+                c[q] = sCnt[lane_id() * 4 + q];
+                sum += c[q];
+            }
+            const int incl = wave_inclusive_scan(sum);
+            const int half = __shfl(incl, kWave / 2 - 1, kWave);
+            int run = incl - sum - (lane_id() >= kWave / 2 ? half : 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sCnt[lane_id() * 4 + q] = run;
+                run += c[q];
+            }
+        }
+        __syncthreads();
+        uint32_t gl = 0xFFFFFFFFu, gh = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            gl = sRedU[w] < gl ? sRedU[w] : gl;
+            gh = sRedU[NW + w] > gh ? sRedU[NW + w] : gh;
+        }
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            if ((blt[e] >> lane_id()) & 1) {
+                const int rank = sCnt[e * NW + wave_id()] + ballot_rank(blt[e]);
+                sKey[rank] = ((uint64_t)st[e] << 32) | (uint32_t)(e * NT + tid);
+            }
+        }
+        __syncthreads();
+        if (c_lt > 1 && gl != gh)  // uniform
+            order_keys<NT, uint64_t>(sKey, c_lt, ~0ull);
+        // the sort uses sKey as its exchange buffer, so the youngest victims
+        // are placed after it
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            if ((beq[e] >> lane_id()) & 1) {
+                const int rank = sCnt[kCntE * NW + e * NW + wave_id()] + ballot_rank(beq[e]);
+                if (rank < m_rem)
+                    sKey[c_lt + rank] = ((uint64_t)st[e] << 32) | (uint32_t)(e * NT + tid);
+            }
+        }
         __syncthreads();
     }
 
     // Commit: hits take the new stamp, victims the missing row and the stamp.
     kvr_fill *fills = a.fills + (int64_t)i * sh.B;
-    for (int idx = tid; idx < nU; idx += NT) {
-        const int32_t s = sSlot[idx];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        if (!((owned >> e) & 1))
+            continue;
+        const uint32_t h = word[e] & kIndexMask;
+        const int32_t s = hval[h];
         if (s >= 0) {
             stamp[s] = now;
         } else {
@@ -445,50 +527,43 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
             const int32_t slot = (int32_t)(uint32_t)sKey[rank];
             if ((uint32_t)slot >= (uint32_t)sh.B)
                 continue;  // cannot happen: every rank below m_total has a victim
-            const int32_t u = sU[idx];
+            const int32_t u = hkey[h];
             tag[slot] = u;
             stamp[slot] = now;
             fills[rank] = kvr_fill{u, slot};
-            sSlot[idx] = slot | kFilledBit;
+            hval[h] = slot | kFilledBit;
         }
     }
     __syncthreads();
 
     // Location words in selection order; count entries by where they were found.
     uint64_t counts = 0;  // 16-bit fields: tail, page, hit, miss
-    {
-        int32_t key[EK];
-        int hidx[EK];
 #pragma unroll
-        for (int e = 0; e < EK; ++e)
-            key[e] = (word[e] == kPending) ? pos[e] : INT_MIN;
-        if (nU > 0)
-            lds_find_many<EK>(sU, nU, key, hidx);
-#pragma unroll
-        for (int e = 0; e < EK; ++e) {
-            const int j = e * NT + tid;
-            if (j >= k)
-                continue;
-            uint32_t w = word[e];
-            if (w == kPending) {
-                const int32_t s = sSlot[hidx[e]];
-                w = (2u << kPlaceShift) | (uint32_t)(s & kIndexMask);
-                counts += (s & kFilledBit) ? (1ull << 48) : (1ull << 32);
-            } else {
-                counts += (w >> kPlaceShift) == 0 ? 1ull : (1ull << 16);
-            }
-            loc[j] = w;
+    for (int e = 0; e < EK; ++e) {
+        const int j = e * NT + tid;
+        if (j >= k)
+            continue;
+        uint32_t w = word[e];
+        if (is_pending(w)) {
+            const int32_t s = hval[w & kIndexMask];
+            w = (2u << kPlaceShift) | (uint32_t)(s & kIndexMask);
+            counts += (s & kFilledBit) ? (1ull << 48) : (1ull << 32);
+        } else {
+            counts += (w >> kPlaceShift) == 0 ? 1ull : (1ull << 16);
         }
+        loc[j] = w;
     }
     if (a.stats) {
-        const uint64_t tot = block_sum<NT>((unsigned long long)counts, sRed);
+        const unsigned long long wsum = wave_sum((unsigned long long)counts);
+        unsigned long long *stp = reinterpret_cast<unsigned long long *>(a.stats);
+        if (lane_id() == 0 && wsum) {
+            atomicAdd(&stp[1], wsum & 0xFFFF);
+            atomicAdd(&stp[2], (wsum >> 16) & 0xFFFF);
+            atomicAdd(&stp[3], (wsum >> 32) & 0xFFFF);
+            atomicAdd(&stp[4], (wsum >> 48) & 0xFFFF);
+        }
         if (tid == 0) {
-            unsigned long long *stp = reinterpret_cast<unsigned long long *>(a.stats);
             atomicAdd(&stp[0], 1ull);
-            atomicAdd(&stp[1], tot & 0xFFFF);
-            atomicAdd(&stp[2], (tot >> 16) & 0xFFFF);
-            atomicAdd(&stp[3], (tot >> 32) & 0xFFFF);
-            atomicAdd(&stp[4], (tot >> 48) & 0xFFFF);
             atomicAdd(&stp[5], (unsigned long long)m_total);
             if (a.count_host_bytes)
                 atomicAdd(&stp[6], (unsigned long long)m_total * (unsigned long long)sh.R);
@@ -501,22 +576,95 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     }
 }
 
-int lds_entries(int n) { return next_pow2(n > NT ? n : NT); }
+// Bound on the kernel's static LDS (histogram, compaction counts, scalars).
+constexpr size_t kStaticLdsBound = 4096;
+constexpr size_t kLdsPerCu = 160 * 1024;
 
 }  // namespace
 
-size_t resolve_lds_bytes(const Shape &sh)
+// Dynamic LDS layout of one resolve workgroup: victim keys then the hash
+// (keys and values).  Returns 0 when the shape does not fit in LDS.
+size_t resolve_lds_layout(const Shape &sh, int32_t *vc, int32_t *hs)
 {
-    return (size_t)lds_entries(sh.B) * 8 + (size_t)lds_entries(sh.sel_cap) * 8;
+    const int m_cap = sh.B < sh.sel_cap ? sh.B : sh.sel_cap;
+    const int v = next_pow2(m_cap > NT ? m_cap : NT);
+    const size_t budget = kLdsPerCu - kStaticLdsBound;
+    if ((size_t)v * 8 >= budget)
+        return 0;
+    size_t h = (budget - (size_t)v * 8) / 8;
+    const size_t want = (size_t)4 * sh.sel_cap > 256 ? (size_t)4 * sh.sel_cap : 256;
+    if (h > want)
+        h = want;
+    h = h / 64 * 64;
+    // keep the load factor at most 0.8 and at least one empty entry
+    if (h < (size_t)sh.sel_cap + (size_t)sh.sel_cap / 4 + 64)
+        return 0;
+    *vc = v;
+    *hs = (int32_t)h;
+    return (size_t)v * 8 + h * 8;
 }
 
+size_t resolve_lds_bytes(const Shape &sh)
+{
+    int32_t vc, hs;
+    return resolve_lds_layout(sh, &vc, &hs);
+}
+
+namespace {
+
+template <int EK, int EB>
+const void *kernel_ptr()
+{
+    return reinterpret_cast<const void *>(&resolve_kernel<EK, EB>);
+}
+
+int per_thread(int n)
+{
+    const int e = (n + NT - 1) / NT;
+    return e <= 1 ? 1 : (e <= 2 ? 2 : (e <= 4 ? 4 : 8));
+}
+
+template <int EK>
+const void *pick_eb(int eb)
+{
+    switch (eb) {
+    case 1: return kernel_ptr<EK, 1>();
+    case 2: return kernel_ptr<EK, 2>();
+    case 4: return kernel_ptr<EK, 4>();
+    default: return kernel_ptr<EK, 8>();
+    }
+}
+
+const void *pick_kernel(const Shape &sh)
+{
+    const int eb = per_thread(sh.B);
+    switch (per_thread(sh.sel_cap)) {
+    case 1: return pick_eb<1>(eb);
+    case 2: return pick_eb<2>(eb);
+    case 4: return pick_eb<4>(eb);
+    default: return pick_eb<8>(eb);
+    }
+}
+
+}  // namespace
+
 // The limit is a per-kernel attribute shared by every context, so it is set
-// to the largest dynamic LDS any valid shape can ask for.
+// to the largest dynamic LDS any shape may use, on every instance.
 hipError_t prepare_resolve_kernel()
 {
-    const size_t most = (size_t)kMaxHotSlots * 8 + (size_t)kMaxSelCap * 8;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&resolve_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    const int most = (int)(kLdsPerCu - kStaticLdsBound);
+    for (int ek = 1; ek <= 8; ek *= 2) {
+        for (int eb = 1; eb <= 8; eb *= 2) {
+            Shape sh{};
+            sh.sel_cap = ek * NT;
+            sh.B = eb * NT;
+            hipError_t e = hipFuncSetAttribute(pick_kernel(sh),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, most);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
@@ -542,10 +690,9 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
     a.fill_count = fill_count;
     a.status = status;
     a.stats = stats;
-    a.u_cap = lds_entries(c->shape.sel_cap);
-    a.b_cap = lds_entries(c->shape.B);
-    hipLaunchKernelGGL(resolve_kernel, dim3(n), dim3(NT), c->resolve_lds, s, a);
-    return hipGetLastError();
+    const size_t lds = resolve_lds_layout(c->shape, &a.vc, &a.hs);
+    void *args[] = {&a};
+    return hipLaunchKernel(pick_kernel(c->shape), dim3(n), dim3(NT), args, lds, s);
 }
 
 }  // namespace kvr

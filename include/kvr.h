@@ -201,7 +201,7 @@ int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32
  * selections, ascending; map[i][qi][j] = index of sel[i][qi][j] in it.
  *   sel (device) int32 [n][q][k]; union_rows (device) int32 [n][q*k];
  *   union_count (device) int32 [n]; map (device) int32 [n][q][k].
- *   Requires q * k <= 16384.  The union is then resolved once. */
+ *   Requires q * k <= 8192.  The union is then resolved once. */
 int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,
                                 int32_t *union_rows, int32_t *union_count, int32_t *map,
                                 void *stream);
