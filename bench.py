@@ -183,10 +183,15 @@ def main():
     snap = gpu.snapshot()
     stats_before = gpu.stats_dict()
 
-    # Pass 1 (eager, same steps): HIP events around every call give the
-    # per-kernel durations (events cannot be recorded inside a graph).
+    # Pass 1 (eager, same steps, same launches): HIP events around every call
+    # give the per-kernel durations (events cannot be recorded inside a
+    # graph); the calls are serialized so each event pair times one kernel
+    # running alone.
     for s in range(W, total):
-        gpu.step(s, timer=timer, prefetch_groups=pg)
+        # a bounded GPU-side spin first, so the whole step is queued before the
+        # GPU reaches it and each event pair brackets only its kernel
+        torch.cuda._sleep(400_000)
+        gpu.step(s, timer=timer, prefetch_groups=pg, serialize=True)
     torch.cuda.synchronize()
     if not args.no_graph:
         gpu.restore(snap)
@@ -248,7 +253,8 @@ def main():
                 "kernel": "gather_kernel", "bytes_per_launch": int(bytes_gather),
                 "launch_us": round(g_ms * 1e3, 2),
                 "timing": "HIP events around each gather launch in an eager pass over the "
-                          "same timed steps from the same starting state"}
+                          "same timed steps and launches from the same starting state, "
+                          "no two kernels overlapping"}
 
     stats_all = gpu.stats_dict()
     stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}

@@ -284,6 +284,143 @@ __device__ void block_sort_lds(K *s, int n, K pad)
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Wave-sort + merge-by-rank: s[0..n) ascending in LDS (ties keep run order,
+// so duplicate keys land in distinct places).  Each 64-lane wave sorts its
+// own run of 64*E keys in registers (bitonic network: strides of 64 and more
+// inside a thread, smaller ones through cross-lane shuffles, no barriers);
+// then every key's final place is its position in its run plus, for every
+// other run, the number of keys of that run that go before it (binary
+// searches, all of a thread's searches interleaved).  `pad` must sort after
+// every real key; keys at or beyond n are not written back.
+
+template <int E, typename K>
+__device__ __forceinline__ void wave_sort_run(K (&v)[E])
+{
+    constexpr int N = kWave * E;
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j >= kWave) {
+                const int je = j / kWave;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if ((e & je) == 0) {
+                        const int idx = e * kWave + lane;
+                        const bool up = (idx & k) == 0;
+                        K a = v[e], b = v[e | je];
+                        if (up ? (a > b) : (a < b)) {
+                            v[e] = b;
+                            v[e | je] = a;
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int idx = e * kWave + lane;
+                    const K o = __shfl_xor(v[e], j, kWave);
+                    const bool keep_min = ((idx & j) == 0) == ((idx & k) == 0);
+                    v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
+                }
+            }
+        }
+    }
+}
+
+template <int NT, int E, typename K>
+__device__ void block_merge_sort_e(K *s, int n, K pad)
+{
+    constexpr int NW = NT / kWave;
+    constexpr int RUN = kWave * E;
+    __shared__ int s_pads;  // real keys equal to pad
+    const int w = wave_id(), lane = lane_id();
+    if (threadIdx.x == 0)
+        s_pads = 0;
+    __syncthreads();
+    K v[E];
+    int pads = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int idx = w * RUN + e * kWave + lane;
+        v[e] = idx < n ? s[idx] : pad;
+        pads += (idx < n && !(v[e] < pad)) ? 1 : 0;
+    }
+    pads = wave_sum(pads);
+    if (lane == 0 && pads)
+        atomicAdd(&s_pads, pads);
+    wave_sort_run<E>(v);
+    __syncthreads();  // every thread has read its keys
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        s[w * RUN + e * kWave + lane] = v[e];
+    __syncthreads();
+    int rank[E];
+    // For every other run, the number of its keys that go before v: runs
+    // before this one count keys <= v (ties go to earlier runs), runs after it
+    // keys < v; "<= v" is "< v + 1" (keys equal to pad are never placed).
+    // The searches into eight runs advance together (eight loads in flight);
+    // one key and eight runs at a time bound the register footprint.
+#pragma unroll 1
+    for (int e = 0; e < E; ++e) {
+        const K lt = v[e];
+        const K le = v[e] < pad ? K(v[e] + 1) : v[e];
+        int r = e * kWave + lane;
+#pragma unroll 1
+        for (int og = 0; og < NW; og += 8) {
+            int lo[8];
+#pragma unroll
+            for (int o = 0; o < 8; ++o)
+                lo[o] = 0;
+#pragma unroll
+            for (int step = RUN / 2; step > 0; step >>= 1) {
+                K x[8];
+#pragma unroll
+                for (int o = 0; o < 8; ++o)
+                    x[o] = s[(og + o) * RUN + lo[o] + step - 1];
+#pragma unroll
+                for (int o = 0; o < 8; ++o)
+                    lo[o] += x[o] < (og + o < w ? le : lt) ? step : 0;
+            }
+#pragma unroll
+            for (int o = 0; o < 8; ++o) {
+                const K x = s[(og + o) * RUN + lo[o]];
+                const int c = lo[o] + (x < (og + o < w ? le : lt) ? 1 : 0);
+                r += og + o == w ? 0 : c;
+            }
+        }
+        rank[e] = r;
+    }
+    const int n_less = n - s_pads;  // real keys below pad take places [0, n_less)
+    __syncthreads();  // every search is done before keys move
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (v[e] < pad && rank[e] < n_less)
+            s[rank[e]] = v[e];
+    for (int t = n_less + (int)threadIdx.x; t < n; t += NT)
+        s[t] = pad;
+    __syncthreads();
+}
+
+// s[0..n) ascending, n <= EMAX * NT; s must hold max(NT, next_pow2(n)) keys.
+// Only run widths up to EMAX * 64 are instantiated (they set the register
+// budget of the calling kernel).
+template <int NT, int EMAX, typename K>
+__device__ void block_merge_sort(K *s, int n, K pad)
+{
+    const int E = next_pow2(n > NT ? n : NT) / NT;
+    if (EMAX <= 1 || E <= 1)
+        block_merge_sort_e<NT, 1, K>(s, n, pad);
+    else if (EMAX <= 2 || E <= 2)
+        block_merge_sort_e<NT, (EMAX >= 2 ? 2 : 1), K>(s, n, pad);
+    else if (EMAX <= 4 || E <= 4)
+        block_merge_sort_e<NT, (EMAX >= 4 ? 4 : 1), K>(s, n, pad);
+    else
+        block_merge_sort_e<NT, (EMAX >= 8 ? 8 : 1), K>(s, n, pad);
+}
+
 // E independent binary searches at once (their LDS reads overlap): idx[e] is
 // the position of key[e] in the ascending s[0..n), or -1.
 template <int E>
@@ -294,17 +431,28 @@ __device__ __forceinline__ void lds_find_many(const int32_t *s, int n, const int
 #pragma unroll
     for (int e = 0; e < E; ++e)
         lo[e] = 0;
+    // loads are unconditional (indices clamped into the array) so that all E
+    // of a round are in flight together
     for (int step = next_pow2(n + 1) >> 1; step > 0; step >>= 1) {
+        int32_t x[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int probe = lo[e] + step - 1;
-            if (probe < n && s[probe] < key[e])
-                lo[e] += step;
+            x[e] = s[probe < n ? probe : 0];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int probe = lo[e] + step - 1;
+            lo[e] += (probe < n && x[e] < key[e]) ? step : 0;
         }
     }
+    int32_t x[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        idx[e] = (lo[e] < n && s[lo[e]] == key[e]) ? lo[e] : -1;
+        x[e] = s[lo[e] < n ? lo[e] : 0];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        idx[e] = (lo[e] < n && x[e] == key[e]) ? lo[e] : -1;
 }
 
 // Index of v in the ascending s[0..n), or -1.

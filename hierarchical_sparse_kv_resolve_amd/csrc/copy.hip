@@ -131,53 +131,62 @@ struct RefillArgs {
     int32_t *status;
 };
 
-// grid: (tiles of B fill rows, requests, layers)
-__global__ __launch_bounds__(NT) void refill_kernel(RefillArgs a)
+// grid: (workers, layers).  Host rows arrive over the host link, so a few
+// workers with many loads in flight keep it busy; a bounded grid leaves the
+// other compute units free for kernels that run beside the fills (the next
+// resolve, gathers of other layers).  Each worker strides over the
+// (request, tile of fill rows) pairs and skips tiles beyond a request's fills.
+__global__ __launch_bounds__(NT) void refill_kernel(RefillArgs a, int32_t n, int32_t tiles_per_req)
 {
     __shared__ const uint8_t *sSrc[kMaxTileRows];
     __shared__ uint8_t *sDst[kMaxTileRows];
-    const int i = blockIdx.y;
-    const int t = blockIdx.z;
-    const int r = a.req_ids ? a.req_ids[i] : i;
-    int fc = a.fill_count[i];
-    fc = fc < 0 ? 0 : (fc > a.sh.B ? a.sh.B : fc);
-    const int j0 = blockIdx.x * a.ts.rows;
-    if (j0 >= fc || r < 0 || r >= a.sh.n_req)
-        return;
-    const int nrows = min(a.ts.rows, fc - j0);
+    const int t = blockIdx.y;
     const int R = a.sh.R;
-    if ((int)threadIdx.x < nrows) {
-        const kvr_fill f = a.fills[(int64_t)i * a.sh.B + j0 + threadIdx.x];
-        const bool ok = f.row >= 0 && (int64_t)f.row < a.sh.host_rows && f.slot >= 0 && f.slot < a.sh.B;
-        sSrc[threadIdx.x] = ok ? a.host[t] + ((int64_t)r * a.sh.host_rows + f.row) * R : nullptr;
-        sDst[threadIdx.x] = ok ? a.hot[t] + ((int64_t)r * a.sh.B + f.slot) * R : nullptr;
-        if (!ok && a.status)
-            a.status[i] = KVR_E_RANGE;
-    }
-    __syncthreads();
     const int C = a.ts.chunks;
-    const int total = nrows * C;
-    for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
-        u32x4 v[kUnroll];
-        uint8_t *dsts[kUnroll];
+    for (int64_t job = blockIdx.x; job < (int64_t)n * tiles_per_req; job += gridDim.x) {
+        const int i = (int)(job / tiles_per_req);
+        const int tile = (int)(job - (int64_t)i * tiles_per_req);
+        const int r = a.req_ids ? a.req_ids[i] : i;
+        int fc = a.fill_count[i];
+        fc = fc < 0 ? 0 : (fc > a.sh.B ? a.sh.B : fc);
+        const int j0 = tile * a.ts.rows;
+        if (j0 >= fc || r < 0 || r >= a.sh.n_req)
+            continue;  // uniform across the workgroup
+        const int nrows = min(a.ts.rows, fc - j0);
+        __syncthreads();  // the previous tile's readers are done with sSrc/sDst
+        if ((int)threadIdx.x < nrows) {
+            const kvr_fill f = a.fills[(int64_t)i * a.sh.B + j0 + threadIdx.x];
+            const bool ok =
+                f.row >= 0 && (int64_t)f.row < a.sh.host_rows && f.slot >= 0 && f.slot < a.sh.B;
+            sSrc[threadIdx.x] = ok ? a.host[t] + ((int64_t)r * a.sh.host_rows + f.row) * R : nullptr;
+            sDst[threadIdx.x] = ok ? a.hot[t] + ((int64_t)r * a.sh.B + f.slot) * R : nullptr;
+            if (!ok && a.status)
+                a.status[i] = KVR_E_RANGE;
+        }
+        __syncthreads();
+        const int total = nrows * C;
+        for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
+            u32x4 v[kUnroll];
+            uint8_t *dsts[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int c = c0 + u * NT + threadIdx.x;
-            dsts[u] = nullptr;
-            if (c < total) {
-                const int row = (int)(((uint64_t)(uint32_t)c * a.ts.magic) >> 32);
-                const uint8_t *src = sSrc[row];
-                if (src) {
-                    const int off = (c - row * C) * 16;
-                    dsts[u] = sDst[row] + off;
-                    load_chunk(v[u], src + off);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int c = c0 + u * NT + threadIdx.x;
+                dsts[u] = nullptr;
+                if (c < total) {
+                    const int row = (int)(((uint64_t)(uint32_t)c * a.ts.magic) >> 32);
+                    const uint8_t *src = sSrc[row];
+                    if (src) {
+                        const int off = (c - row * C) * 16;
+                        dsts[u] = sDst[row] + off;
+                        load_chunk(v[u], src + off);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (dsts[u])
-                store_chunk(dsts[u], v[u]);
+            for (int u = 0; u < kUnroll; ++u)
+                if (dsts[u])
+                    store_chunk(dsts[u], v[u]);
+        }
     }
 }
 
@@ -308,6 +317,9 @@ hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t 
     return hipSuccess;
 }
 
+// Workers per refill launch, over all its layers.
+constexpr int kRefillWorkers = 128;
+
 hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_layers, int32_t n,
                          const int32_t *req_ids, const kvr_fill *fills, const int32_t *fill_count,
                          int32_t *status, hipStream_t s)
@@ -319,14 +331,18 @@ hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_laye
     a.fills = fills;
     a.fill_count = fill_count;
     a.status = status;
+    const int tiles_per_req = (c->shape.B + a.ts.rows - 1) / a.ts.rows;
     for (int32_t t0 = 0; t0 < n_layers; t0 += kGatherLayersPerLaunch) {
         const int nt = n_layers - t0 < kGatherLayersPerLaunch ? n_layers - t0 : kGatherLayersPerLaunch;
         for (int t = 0; t < nt; ++t) {
             a.hot[t] = c->layers_h[layers[t0 + t]].hot;
             a.host[t] = c->layers_h[layers[t0 + t]].host;
         }
-        dim3 grid((c->shape.B + a.ts.rows - 1) / a.ts.rows, n, nt);
-        hipLaunchKernelGGL(refill_kernel, grid, dim3(NT), 0, s, a);
+        const int64_t jobs = (int64_t)n * tiles_per_req;
+        int64_t workers = (kRefillWorkers + nt - 1) / nt;
+        workers = workers < jobs ? workers : jobs;
+        dim3 grid((unsigned)(workers > 0 ? workers : 1), nt);
+        hipLaunchKernelGGL(refill_kernel, grid, dim3(NT), 0, s, a, n, tiles_per_req);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -27,8 +27,8 @@
 // the first candidates stamped tau in slot order (ordered compaction with
 // wave ballots).  Only the candidates older than tau are sorted, and only
 // when their stamps differ.  Misses take victims in ascending row order.
-// Up to 1024 keys are put in order by counting (one broadcast pass over LDS),
-// more by the register/shuffle bitonic network.
+// Up to 256 keys are put in order by counting ranks; more by sorting a run
+// per wave in registers and merging the runs by rank (block_merge_sort).
 #include <climits>
 
 #include "block.h"
@@ -96,11 +96,10 @@ __device__ __forceinline__ int hinsert(int32_t *hkey, int hs, int32_t key, bool 
     }
 }
 
-// Ascending order of n <= NT distinct keys s[0..n) in place, by counting for
-// each key the keys below it (no sorting network).  P = NT / next_pow2(n)
-// consecutive lanes share one key and split the count, so each thread reads
-// about n * n / NT keys; the partial counts meet through shuffles.  Every
-// thread of the workgroup must call it.
+// Ascending order of n <= 256 distinct keys s[0..n) in place, by counting for
+// each key the keys below it.  P = NT / next_pow2(n) consecutive lanes share
+// one key and split the count over contiguous chunks (eight independent LDS
+// reads in flight per round); the partial counts meet through shuffles.
 template <int NT, typename K>
 __device__ __forceinline__ void rank_sort_small(K *s, int n)
 {
@@ -109,8 +108,21 @@ __device__ __forceinline__ void rank_sort_small(K *s, int n)
     P = P > kWave ? kWave : P;
     const int el = tid / P, part = tid % P;
     const K mine = el < n ? s[el] : K(0);
+    const int chunk = (n + P - 1) / P;
+    const int j0 = part * chunk;
+    const int j1 = j0 + chunk < n ? j0 + chunk : n;
     int below = 0;
-    for (int j = part; j < n; j += P)
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+        K v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = s[j + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            below += v[q] < mine ? 1 : 0;
+    }
+    for (; j < j1; ++j)
         below += s[j] < mine ? 1 : 0;
     for (int d = 1; d < P; d <<= 1)
         below += __shfl_xor(below, d, kWave);
@@ -120,19 +132,9 @@ __device__ __forceinline__ void rank_sort_small(K *s, int n)
     __syncthreads();
 }
 
-// Ascending order of s[0..n) of distinct keys: counting for small n, the
-// bitonic network otherwise.
-template <int NT, typename K>
-__device__ __forceinline__ void order_keys(K *s, int n, K pad)
-{
-    if (n <= NT)
-        rank_sort_small<NT, K>(s, n);
-    else
-        block_sort_lds<NT, K>(s, n, pad);
-}
-
 // E lookups with interleaved probes: idx[e] = entry of key[e], or -1 when it
-// is absent or key[e] < 0.
+// is absent or key[e] < 0.  Each round issues all E loads before using any
+// (finished lookups re-read their last entry), so their latencies overlap.
 template <int E>
 __device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const int32_t (&key)[E],
                                            int (&idx)[E])
@@ -145,24 +147,24 @@ __device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const in
         cur[e] = live[e] ? hslot(key[e], hs) : 0;
         idx[e] = -1;
     }
-    bool any = true;
-    while (any) {
-        any = false;
+    while (true) {
+        int32_t kk[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            kk[e] = hkey[cur[e]];
+        bool any = false;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            if (live[e]) {
-                const int32_t kk = hkey[cur[e]];
-                if (kk == key[e]) {
-                    idx[e] = cur[e];
-                    live[e] = false;
-                } else if (kk == kEmpty) {
-                    live[e] = false;
-                } else {
-                    cur[e] = hnext(cur[e], hs);
-                    any = true;
-                }
-            }
+            const bool hit = live[e] && kk[e] == key[e];
+            const bool stop = hit || kk[e] == kEmpty;
+            idx[e] = hit ? cur[e] : idx[e];
+            live[e] = live[e] && !stop;
+            const int nxt = cur[e] + 1 == hs ? 0 : cur[e] + 1;
+            cur[e] = live[e] ? nxt : cur[e];
+            any = any || live[e];
         }
+        if (!any)
+            break;
     }
 }
 
@@ -197,7 +199,6 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     __shared__ int sMiss;
     __shared__ int sRangeErr;
     __shared__ int sHostErr;
-    __shared__ int sTagSink;
 
     const Shape &sh = a.sh;
     const int i = blockIdx.x;
@@ -214,7 +215,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     int32_t *tag = a.tag + (int64_t)r * sh.B;
     uint32_t *stamp = a.stamp + (int64_t)r * sh.B;
 
-    // Tags and stamps of this thread's slots (slot b = e*NT + tid), issued first.
+    // The selection rows (head of the longest dependent chain: row -> page
+    // map), then the tags and stamps of this thread's slots (b = e*NT + tid).
+    int32_t p_in[EK];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        const int j = e * NT + tid;
+        p_in[e] = j < k ? sel[j] : 0;
+    }
     int32_t t[EB];
     uint32_t st[EB];
 #pragma unroll
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     for (int e = 0; e < EK; ++e) {
         const int j = e * NT + tid;
         if (j < k) {
-            const int32_t p = sel[j];
+            const int32_t p = p_in[e];
             if (p < 0 || p >= L) {
                 sRangeErr = 1;
             } else if (p >= tail_lo) {
@@ -294,14 +302,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         }
         lo = wave_min(lo);
         hi = wave_max(hi);
-        tmax = wave_max(tmax);
+        // tmax is never used: consuming it here makes the tag loads complete
+        // inside step 1 instead of being sunk to their first use
+        asm volatile("; tags in %0" ::"v"(tmax));
         if (lane_id() == 0) {
             if (wf)
                 atomicAdd(&sUnique, wf);
             sRedU[wave_id()] = lo;
             sRedU[NW + wave_id()] = hi;
-            if (wave_id() == 0)
-                sTagSink = tmax;
         }
     }
     __syncthreads();
@@ -339,15 +347,16 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     // Misses: pending rows no slot holds (each checked once, by the entry that
     // inserted it); each needs a host copy.  The list packs (row, hash entry).
     uint64_t *sMissList = sKey;
+    int32_t hv[EK];
+#pragma unroll
+    for (int e = 0; e < EK; ++e)
+        hv[e] = hval[((owned >> e) & 1) ? (word[e] & kIndexMask) : 0];
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
-        bool miss = false;
         const uint32_t h = word[e] & kIndexMask;
-        if ((owned >> e) & 1) {
-            miss = hval[h] == kNoSlot;
-            if (miss && ((nohost >> e) & 1))
-                sHostErr = 1;
-        }
+        const bool miss = ((owned >> e) & 1) && hv[e] == kNoSlot;
+        if (miss && ((nohost >> e) & 1))
+            sHostErr = 1;
         const uint64_t mb = __ballot(miss);
         int wbase = 0;
         if (lane_id() == 0 && mb)
@@ -364,19 +373,58 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     const int m_total = sMiss;
 
     if (m_total > 0) {
-        // Misses in ascending row order; each learns its rank.
-        order_keys<NT, uint64_t>(sMissList, m_total, ~0ull);
-        for (int q = tid; q < m_total; q += NT)
-            hval[(uint32_t)sMissList[q]] = -1 - q;
+        // Misses in ascending row order (wave-sorted runs merged by rank);
+        // each learns its rank through the hash entry packed with its row.
+        if (m_total <= 256) {
+            rank_sort_small<NT, uint64_t>(sMissList, m_total);
+            for (int q = tid; q < m_total; q += NT)
+                hval[(uint32_t)sMissList[q]] = -1 - q;
+        } else {
+            // plain rows sort cheaper; each then finds its entry in the hash
+            int32_t *rows = reinterpret_cast<int32_t *>(sMissList);
+            uint32_t own[EK];
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                const int q = e * NT + tid;
+                own[e] = q < m_total ? (uint32_t)(sMissList[q] >> 32) : 0u;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                const int q = e * NT + tid;
+                if (q < m_total)
+                    rows[q] = (int32_t)own[e];
+            }
+            __syncthreads();
+            block_merge_sort<NT, (EK < EB ? EK : EB), int32_t>(rows, m_total, INT_MAX);
+            int32_t key[EK];
+            int idx[EK];
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                const int q = e * NT + tid;
+                key[e] = q < m_total ? rows[q] : -1;
+            }
+            hfind_many<EK>(hkey, hs, key, idx);
+#pragma unroll
+            for (int e = 0; e < EK; ++e)
+                if (idx[e] >= 0)
+                    hval[idx[e]] = -1 - (e * NT + tid);
+        }
         __syncthreads();
 
         // Step 3: victims = the m_total smallest (stamp, slot) among the slots
         // whose tag is not a hit of this call.
         bool cand[EB];
+        {
+            int32_t hs_[EB];
 #pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            const int b = e * NT + tid;
-            cand[e] = b < sh.B && !(fidx[e] >= 0 && hval[fidx[e]] == b);
+            for (int e = 0; e < EB; ++e)
+                hs_[e] = hval[fidx[e] >= 0 ? fidx[e] : 0];
+#pragma unroll
+            for (int e = 0; e < EB; ++e) {
+                const int b = e * NT + tid;
+                cand[e] = b < sh.B && !(fidx[e] >= 0 && hs_[e] == b);
+            }
         }
         // Radix select of the threshold stamp over rel = stamp - lo, 8 bits
         // at a time from the highest digit that varies.
@@ -497,8 +545,51 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
             }
         }
         __syncthreads();
-        if (c_lt > 1 && gl != gh)  // uniform
-            order_keys<NT, uint64_t>(sKey, c_lt, ~0ull);
+        if (c_lt > 1 && gl != gh) {  // uniform
+            if (c_lt <= 256) {
+                rank_sort_small<NT, uint64_t>(sKey, c_lt);
+            } else if (gh - gl < (1u << 18)) {
+                // (stamp - gl, slot) packs into 31 bits: sort those instead
+                int32_t *k32 = reinterpret_cast<int32_t *>(sKey);
+                uint64_t own[EB];
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int q = e * NT + tid;
+                    own[e] = q < c_lt ? sKey[q] : 0ull;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int q = e * NT + tid;
+                    if (q < c_lt)
+                        k32[q] = (int32_t)(((uint32_t)(own[e] >> 32) - gl) << 13 | (uint32_t)own[e]);
+                }
+                __syncthreads();
+                block_merge_sort<NT, (EK < EB ? EK : EB), int32_t>(k32, c_lt, INT_MAX);
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int q = e * NT + tid;
+                    own[e] = q < c_lt ? (uint64_t)(uint32_t)k32[q] : 0ull;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int q = e * NT + tid;
+                    if (q < c_lt)
+                        sKey[q] = ((uint64_t)((uint32_t)(own[e] >> 13) + gl) << 32) |
+                                  (uint32_t)(own[e] & 0x1FFF);
+                }
+                __syncthreads();
+            } else {
+                // stamps more than 2^18 ticks apart: the in-LDS network
+                // (slow, rare, light on registers)
+                const int width = next_pow2(c_lt);
+                for (int q = c_lt + tid; q < width; q += NT)
+                    sKey[q] = ~0ull;
+                __syncthreads();
+                bitonic_sort<NT>(sKey, width);
+            }
+        }
         // the sort uses sKey as its exchange buffer, so the youngest victims
         // are placed after it
 #pragma unroll
@@ -515,11 +606,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     // Commit: hits take the new stamp, victims the missing row and the stamp.
     kvr_fill *fills = a.fills + (int64_t)i * sh.B;
 #pragma unroll
+    for (int e = 0; e < EK; ++e)
+        hv[e] = hval[((owned >> e) & 1) ? (word[e] & kIndexMask) : 0];
+#pragma unroll
     for (int e = 0; e < EK; ++e) {
         if (!((owned >> e) & 1))
             continue;
         const uint32_t h = word[e] & kIndexMask;
-        const int32_t s = hval[h];
+        const int32_t s = hv[e];
         if (s >= 0) {
             stamp[s] = now;
         } else {
@@ -539,13 +633,16 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     // Location words in selection order; count entries by where they were found.
     uint64_t counts = 0;  // 16-bit fields: tail, page, hit, miss
 #pragma unroll
+    for (int e = 0; e < EK; ++e)
+        hv[e] = hval[is_pending(word[e]) ? (word[e] & kIndexMask) : 0];
+#pragma unroll
     for (int e = 0; e < EK; ++e) {
         const int j = e * NT + tid;
         if (j >= k)
             continue;
         uint32_t w = word[e];
         if (is_pending(w)) {
-            const int32_t s = hval[w & kIndexMask];
+            const int32_t s = hv[e];
             w = (2u << kPlaceShift) | (uint32_t)(s & kIndexMask);
             counts += (s & kFilledBit) ? (1ull << 48) : (1ull << 32);
         } else {

@@ -124,20 +124,24 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, timer=None, prefetch_groups: int = 0):
+    def step(self, s: int, timer=None, prefetch_groups: int = 0, serialize: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
 
         prefetch_groups = 0: resolve fills payload layer 0 from host, one
         replay call fills the other layers, one gather call covers them all.
-        prefetch_groups = G > 0 (layers with shared indices and distinct
-        payloads): the host fills of all layers are issued on a side stream in
-        G groups of layers, and each group's gather starts on the current
-        stream as soon as that group's fills are in, so host-link traffic of
-        later groups overlaps the HBM traffic of earlier gathers.
+        prefetch_groups = G > 0: with shared indices and distinct payloads the
+        host fills of all layers are issued on a side stream in G groups of
+        layers, and each group's gather starts on the current stream as soon
+        as that group's fills are in, so host-link traffic of later groups
+        overlaps the HBM traffic of earlier gathers.  With one physical source
+        and several resolving layers, each layer's fill and gather run on the
+        side stream while the next layer resolves.
 
         `timer(name, stream)` may return a context manager that brackets a
-        call with events (used by the benchmark)."""
+        call with events (used by the benchmark).  serialize=True issues the
+        same launches but lets no two of them overlap, so each call's events
+        time that kernel alone."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
         tm = timer or _no_timer
@@ -155,12 +159,35 @@ class GpuRun:
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            pipelined = prefetch_groups > 0 and cfg.reuse == "distinct"
+            pipelined = prefetch_groups > 0
             fill_layer = -1 if (timer or pipelined) else 0
             with tm("resolve", main):
                 ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
                                  self.status[g], self.stats, stream=main)
-            if cfg.reuse != "distinct":
+            if cfg.reuse != "distinct" and prefetch_groups > 0:
+                # One physical source: this layer's fill and gather run on the
+                # side stream while the main stream resolves the next layer
+                # (resolve touches metadata only).  The side stream keeps the
+                # next fill behind this gather: its victims may be slots this
+                # gather still reads.
+                resolved = torch.cuda.Event()
+                resolved.record(main)
+                side = self._side()
+                side.wait_event(resolved)
+                with tm("refill", side):
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
+                                        count, stride, fills, fc, stream=side)
+                with tm("gather", side):
+                    ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
+                                    self.gather_status, stream=side)
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=side)
+                if g == cfg.groups - 1 or serialize:
+                    done = torch.cuda.Event()
+                    done.record(side)
+                    main.wait_event(done)
+            elif cfg.reuse != "distinct":
                 if fill_layer < 0:
                     with tm("refill", main):
                         ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
@@ -194,6 +221,8 @@ class GpuRun:
                     ev = torch.cuda.Event()
                     ev.record(side)
                     ready.append(ev)
+                if serialize:
+                    ready = [ready[-1]] * len(ready)  # every fill before the first gather
                 for grp, ev in zip(groups, ready):
                     main.wait_event(ev)
                     with tm("gather", main):

@@ -116,12 +116,16 @@ def test_full_workload_parity(c):
 
 @pytest.mark.parametrize("groups", [1, 2, 3, 8])
 def test_prefetch_pipeline_parity(groups):
-    """Host fills on a side stream in layer groups, gathers as groups complete:
-    the schedule the benchmark times, same results as the one-stream schedule."""
+    """Host fills on a side stream in layer groups, gathers as groups complete
+    (and, for one physical source, each layer's fill and gather overlapping
+    the next layer's resolve): the schedules the benchmark times, same
+    results as the one-stream schedule."""
     _run_parity(tiny(2), prefetch_groups=groups)
     _run_parity(tiny(4), prefetch_groups=groups)
+    _run_parity(tiny(5), prefetch_groups=groups)
     if groups == 2:
         _run_parity(FULL[2], prefetch_groups=groups)
+        _run_parity(FULL[5], reqs=[0, 63], prefetch_groups=groups)
 
 
 def test_full_long_context_parity_sampled():
@@ -183,7 +187,8 @@ def test_gather_alone_random_locations():
     gpu.close()
 
 
-@pytest.mark.parametrize("q,k", [(1, 1), (4, 90), (3, 1000), (4, 2048), (2, 4096), (5, 0)])
+@pytest.mark.parametrize("q,k", [(1, 1), (4, 90), (3, 1000), (4, 2048), (2, 4096), (5, 0),
+                                 (3, 333), (8, 1024)])
 def test_dedup_alone(q, k):
     import torch
     cfg = tiny(4)
@@ -195,6 +200,10 @@ def test_dedup_alone(q, k):
     if k:
         sel[0, :, :] = sel[0, 0, 0]          # all equal
         sel[1, -1] = sel[1, 0][::-1]           # a permuted duplicate query
+        # extreme values, including the sort's padding value
+        flat = sel[2].reshape(-1)
+        flat[rng.integers(0, flat.size, 5)] = np.iinfo(np.int32).max
+        flat[rng.integers(0, flat.size, 3)] = np.iinfo(np.int32).min
     un = torch.empty((n, q * k), dtype=torch.int32, device="cuda")
     uc = torch.empty(n, dtype=torch.int32, device="cuda")
     mp = torch.empty((n, q, k), dtype=torch.int32, device="cuda")
@@ -328,37 +337,39 @@ def test_closed_form_bytes_full_glm_shape():
 # ------------------------------------------------------------------ HIP graphs
 
 
-@pytest.mark.parametrize("prefetch_groups", [0, 2])
-def test_graph_replays_match_oracle(prefetch_groups):
+@pytest.mark.parametrize("shape,prefetch_groups", [(2, 0), (2, 2), (5, 2), (4, 2)])
+def test_graph_replays_match_oracle(shape, prefetch_groups):
     """Decode steps captured into HIP graphs give the oracle's results: a
     multi-step graph replayed once, then a one-step graph replayed three times
     (each replay is another decode step on the evolving state), with eager
     read-backs and synchronisation between replays."""
     import torch
-    cfg = tiny(2).with_(steps=8)
-    inputs = Inputs(cfg)
+    cfg = tiny(shape).with_(steps=8)
+    inputs = Inputs(cfg, max_new=10)
     gpu = _gpu_run(inputs)
     run = OracleRun(inputs)
     reqs = list(range(cfg.n_req))
+
+    def compare(o):
+        for g in range(cfg.groups):
+            _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
+        _compare_state(gpu, run, reqs)
+
     try:
         gpu.stage(range(cfg.steps))
         gpu.step(0, prefetch_groups=prefetch_groups)
-        o = run.step(0)
-        _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
+        compare(run.step(0))
         g = gpu.capture(range(1, 4), prefetch_groups=prefetch_groups)
         g.replay()
         torch.cuda.synchronize()
         for s in range(1, 4):
             o = run.step(s)
-        _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
-        _compare_state(gpu, run, reqs)
+        compare(o)
         one = gpu.capture([4], prefetch_groups=prefetch_groups)
         for rep in range(3):
             one.replay()
             torch.cuda.synchronize()
-            o = run.step(4)  # the same inputs again: one more row, same selection
-            _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
-            _compare_state(gpu, run, reqs)
+            compare(run.step(4))  # the same inputs again: one more row, same selection
             assert (gpu.gather_status.cpu().numpy() == 0).all()
         for l in range(cfg.payload_layers):
             assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l])
