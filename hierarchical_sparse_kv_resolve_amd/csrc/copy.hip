@@ -1,122 +1,15 @@
-// Byte-moving kernels of the resolver: the gather into contiguous
-// per-request buffers, the host refill of hot-cache slots (also the per-layer
-// replay for shared indices with distinct payloads), the tail append, and
-// small state kernels.
-//
-// Rows are opaque R-byte payloads (R a multiple of 16).  A workgroup owns a
-// tile of whole rows; the rows' source and destination addresses are staged
-// in LDS once, then the tile is moved as a flat run of 16-byte chunks spread
-// over all lanes, with every load of a thread issued before its stores so
-// that several 16-byte requests per lane are in flight.  Rows of 1152 B (72
-// chunks) or 656 B (41 chunks) therefore never leave lanes idle the way a
-// one-row-per-wave mapping would.  Host rows are read straight from pinned
-// memory through its device mapping (zero copy over the host link).
-#include "block.h"
+// Byte-moving kernels of the resolver besides the gather: the host refill of
+// hot-cache slots (also the per-layer replay for shared indices with distinct
+// payloads), the tail append, and small state kernels.  Host rows are read
+// straight from pinned memory through its device mapping (zero copy over the
+// host link), in the same tiles of whole rows as the gather.
 #include "kvr_internal.h"
+#include "rows.h"
 
 namespace kvr {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int NT = 256;
-constexpr int kUnroll = 8;
-constexpr int kMaxTileRows = 128;
-
-struct TileShape {
-    int32_t rows;    // rows per workgroup tile
-    int32_t chunks;  // 16-byte chunks per row
-    uint64_t magic;  // row = (chunk * magic) >> 32 for chunk < rows * chunks
-};
-
-__device__ __forceinline__ void load_chunk(u32x4 &v, const uint8_t *p)
-{
-    v = *reinterpret_cast<const u32x4 *>(p);
-}
-
-__device__ __forceinline__ void store_chunk_nt(uint8_t *p, const u32x4 &v)
-{
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-
-__device__ __forceinline__ void store_chunk(uint8_t *p, const u32x4 &v)
-{
-    *reinterpret_cast<u32x4 *>(p) = v;
-}
-
-// ------------------------------------------------------------------ gather
-
-struct GatherArgs {
-    Shape sh;
-    TileShape ts;
-    const LayerPtrs *layers;  // device table
-    int32_t layer[kGatherLayersPerLaunch];
-    uint8_t *out[kGatherLayersPerLaunch];
-    const int32_t *req_ids;
-    const uint32_t *loc;
-    const int32_t *count;
-    int32_t stride;
-    int32_t *status;
-};
-
-__global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
-{
-    __shared__ const uint8_t *sSrc[kMaxTileRows];
-    const int i = blockIdx.y;
-    const int t = blockIdx.z;
-    const int r = a.req_ids ? a.req_ids[i] : i;
-    int cnt = a.count ? a.count[i] : a.stride;
-    cnt = cnt < 0 ? 0 : (cnt > a.stride ? a.stride : cnt);
-    const int j0 = blockIdx.x * a.ts.rows;
-    if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
-        return;
-    const int nrows = min(a.ts.rows, cnt - j0);
-    const LayerPtrs lp = a.layers[a.layer[t]];
-    const int R = a.sh.R;
-    if ((int)threadIdx.x < nrows) {
-        const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
-        const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
-        const uint8_t *src = nullptr;
-        if (w != KVR_LOC_INVALID) {
-            if (place == KVR_PLACE_TAIL && idx < (uint32_t)a.sh.T)
-                src = lp.tail + ((int64_t)r * a.sh.T + idx) * R;
-            else if (place == KVR_PLACE_PAGE && (int64_t)idx < a.sh.pool_rows)
-                src = lp.pool + (int64_t)idx * R;
-            else if (place == KVR_PLACE_HOT && idx < (uint32_t)a.sh.B)
-                src = lp.hot + ((int64_t)r * a.sh.B + idx) * R;
-            else if (a.status)
-                a.status[i] = KVR_E_RANGE;
-        }
-        sSrc[threadIdx.x] = src;
-    }
-    __syncthreads();
-    uint8_t *dst = a.out[t] + ((int64_t)i * a.stride + j0) * R;
-    const int C = a.ts.chunks;
-    const int total = nrows * C;
-    for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
-        u32x4 v[kUnroll];
-        const uint8_t *srcs[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int c = c0 + u * NT + threadIdx.x;
-            srcs[u] = nullptr;
-            if (c < total) {
-                const int row = (int)(((uint64_t)(uint32_t)c * a.ts.magic) >> 32);
-                const uint8_t *s = sSrc[row];
-                if (s) {
-                    srcs[u] = s;
-                    load_chunk(v[u], s + (c - row * C) * 16);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int c = c0 + u * NT + threadIdx.x;
-            if (srcs[u])
-                store_chunk_nt(dst + (int64_t)c * 16, v[u]);
-        }
-    }
-}
+constexpr int NT = kRowThreads;
 
 // ------------------------------------------------------------------ refill
 
@@ -266,16 +159,6 @@ __global__ void copy_loc_kernel(const uint32_t *src, uint32_t *dst, const int32_
         dst[(int64_t)i * stride + j] = src[(int64_t)i * stride + j];
 }
 
-TileShape tile_for(const Shape &sh)
-{
-    TileShape ts;
-    ts.chunks = sh.R / 16;
-    int rows = (NT * kUnroll) / ts.chunks;
-    ts.rows = rows < 1 ? 1 : (rows > kMaxTileRows ? kMaxTileRows : rows);
-    ts.magic = (((uint64_t)1 << 32) + ts.chunks - 1) / ts.chunks;
-    return ts;
-}
-
 }  // namespace
 
 bool tile_magic_exact(int32_t row_bytes)
@@ -287,34 +170,6 @@ bool tile_magic_exact(int32_t row_bytes)
         if ((uint32_t)(((uint64_t)c * ts.magic) >> 32) != c / (uint32_t)ts.chunks)
             return false;
     return true;
-}
-
-hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t n_targets,
-                         int32_t n, const int32_t *req_ids, const uint32_t *loc,
-                         const int32_t *count, int32_t stride, int32_t *status, hipStream_t s)
-{
-    GatherArgs a;
-    a.sh = c->shape;
-    a.ts = tile_for(c->shape);
-    a.layers = c->layers_d;
-    a.req_ids = req_ids;
-    a.loc = loc;
-    a.count = count;
-    a.stride = stride;
-    a.status = status;
-    for (int32_t t0 = 0; t0 < n_targets; t0 += kGatherLayersPerLaunch) {
-        const int nt = n_targets - t0 < kGatherLayersPerLaunch ? n_targets - t0 : kGatherLayersPerLaunch;
-        for (int t = 0; t < nt; ++t) {
-            a.layer[t] = targets[t0 + t].layer;
-            a.out[t] = targets[t0 + t].out;
-        }
-        dim3 grid((stride + a.ts.rows - 1) / a.ts.rows, n, nt);
-        hipLaunchKernelGGL(gather_kernel, grid, dim3(NT), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
 }
 
 // Workers per refill launch, over all its layers.
@@ -342,8 +197,8 @@ hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_laye
         int64_t workers = (kRefillWorkers + nt - 1) / nt;
         workers = workers < jobs ? workers : jobs;
         dim3 grid((unsigned)(workers > 0 ? workers : 1), nt);
-        hipLaunchKernelGGL(refill_kernel, grid, dim3(NT), 0, s, a, n, tiles_per_req);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch(c, KVR_KERNEL_REFILL, refill_kernel, grid, dim3(NT), 0, s, a, n,
+                              tiles_per_req);
         if (e != hipSuccess)
             return e;
     }
@@ -361,8 +216,7 @@ hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,
     a.req_ids = req_ids;
     a.new_rows = new_rows;
     a.status = status;
-    hipLaunchKernelGGL(append_kernel, dim3(n), dim3(NT), 0, s, a);
-    return hipGetLastError();
+    return launch(c, KVR_KERNEL_APPEND, append_kernel, dim3(n), dim3(NT), 0, s, a);
 }
 
 hipError_t launch_init_state(const kvr_ctx *c, hipStream_t s)
@@ -370,18 +224,16 @@ hipError_t launch_init_state(const kvr_ctx *c, hipStream_t s)
     const int64_t n = (int64_t)c->shape.n_req * c->shape.B;
     int blocks = (int)((n + 255) / 256);
     blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
-    hipLaunchKernelGGL(init_state_kernel, dim3(blocks), dim3(256), 0, s, c->shape, c->L, c->tag,
-                       c->stamp, c->clock);
-    return hipGetLastError();
+    return launch(c, KVR_KERNEL_STATE, init_state_kernel, dim3(blocks), dim3(256), 0, s, c->shape,
+                  c->L, c->tag, c->stamp, c->clock);
 }
 
 hipError_t launch_copy_loc(const kvr_ctx *c, int32_t n, const uint32_t *src, uint32_t *dst,
                            const int32_t *count, int32_t stride, hipStream_t s)
 {
-    (void)c;
     dim3 grid((stride + 255) / 256, n);
-    hipLaunchKernelGGL(copy_loc_kernel, grid, dim3(256), 0, s, src, dst, count, stride);
-    return hipGetLastError();
+    return launch(c, KVR_KERNEL_STATE, copy_loc_kernel, grid, dim3(256), 0, s, src, dst, count,
+                  stride);
 }
 
 }  // namespace kvr

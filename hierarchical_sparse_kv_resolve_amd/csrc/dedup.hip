@@ -155,14 +155,13 @@ hipError_t prepare_dedup_kernel()
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
 }
 
-hipError_t launch_dedup(int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
-                        int32_t *union_count, int32_t *map, hipStream_t s)
+hipError_t launch_dedup(const kvr_ctx *c, int32_t n, int32_t q, int32_t k, const int32_t *sel,
+                        int32_t *union_rows, int32_t *union_count, int32_t *map, hipStream_t s)
 {
     int32_t hs;
     const size_t lds = dedup_layout(q * k, &hs);
-    hipLaunchKernelGGL(dedup_kernel, dim3(n), dim3(NT), lds, s, q, k, hs, sel, union_rows,
-                       union_count, map);
-    return hipGetLastError();
+    return launch(c, KVR_KERNEL_DEDUP, dedup_kernel, dim3(n), dim3(NT), lds, s, q, k, hs, sel,
+                  union_rows, union_count, map);
 }
 
 }  // namespace kvr

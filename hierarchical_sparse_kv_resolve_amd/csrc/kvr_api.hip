@@ -11,7 +11,43 @@
 
 namespace kvr {
 bool tile_magic_exact(int32_t row_bytes);
+
+bool next_timing_events(const kvr_ctx *c, int32_t kind, hipStream_t s, hipEvent_t *start,
+                        hipEvent_t *stop)
+{
+    LaunchLog *t = c ? c->timing : nullptr;
+    if (!t || !t->on)
+        return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return false;
+    if (t->n >= t->limit) {
+        ++t->missed;
+        return false;
+    }
+    t->kind[t->n] = kind;
+    *start = t->ev[2 * t->n];
+    *stop = t->ev[2 * t->n + 1];
+    ++t->n;
+    return true;
 }
+
+namespace {
+
+void free_timing(LaunchLog *t)
+{
+    if (!t)
+        return;
+    for (int32_t i = 0; i < 2 * t->cap; ++i)
+        if (t->ev[i])
+            (void)hipEventDestroy(t->ev[i]);
+    delete[] t->ev;
+    delete[] t->kind;
+    delete t;
+}
+
+}  // namespace
+}  // namespace kvr
 
 namespace {
 
@@ -174,6 +210,7 @@ int kvr_destroy(kvr_ctx *ctx)
         (void)hipFree(ctx->layers_d);
     delete[] ctx->layers_h;
     delete[] ctx->layer_bound;
+    kvr::free_timing(ctx->timing);
     delete ctx;
     return ok();
 }
@@ -353,7 +390,7 @@ int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, c
         return rc;
     if (n == 0)
         return ok();
-    hipError_t e = kvr::launch_dedup(n, q, k, sel, union_rows, union_count, map, s);
+    hipError_t e = kvr::launch_dedup(ctx, n, q, k, sel, union_rows, union_count, map, s);
     return e == hipSuccess ? ok() : hip_fail(e, "dedup launch");
 }
 
@@ -439,6 +476,73 @@ int kvr_host_free(void *ptr)
         return ok();
     hipError_t e = hipHostFree(ptr);
     return e == hipSuccess ? ok() : hip_fail(e, "hipHostFree");
+}
+
+int kvr_timing_begin(kvr_ctx *ctx, int32_t capacity)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    if (capacity < 1 || capacity > (1 << 20))
+        return fail(KVR_E_ARG, "timing capacity %d outside [1, 1048576]", capacity);
+    if (int rc = check_stream(ctx, nullptr))
+        return rc;
+    kvr::LaunchLog *t = ctx->timing;
+    if (!t || t->cap < capacity) {
+        kvr::free_timing(t);
+        ctx->timing = nullptr;
+        t = new (std::nothrow) kvr::LaunchLog();
+        if (!t)
+            return fail(KVR_E_ARG, "out of host memory");
+        t->ev = new (std::nothrow) hipEvent_t[2 * (size_t)capacity]();
+        t->kind = new (std::nothrow) int32_t[capacity]();
+        if (!t->ev || !t->kind) {
+            kvr::free_timing(t);
+            return fail(KVR_E_ARG, "out of host memory");
+        }
+        t->cap = capacity;
+        for (int32_t i = 0; i < 2 * capacity; ++i) {
+            hipError_t e = hipEventCreate(&t->ev[i]);
+            if (e != hipSuccess) {
+                t->ev[i] = nullptr;
+                kvr::free_timing(t);
+                return hip_fail(e, "hipEventCreate");
+            }
+        }
+        ctx->timing = t;
+    }
+    t->limit = capacity;
+    t->n = 0;
+    t->missed = 0;
+    t->on = true;
+    return ok();
+}
+
+int kvr_timing_end(kvr_ctx *ctx, int32_t capacity, int32_t *kinds, float *ms, int32_t *n_recorded)
+{
+    if (int rc = check_ctx(ctx, false))
+        return rc;
+    kvr::LaunchLog *t = ctx->timing;
+    if (!t || !t->on)
+        return fail(KVR_E_ARG, "timing was not started");
+    t->on = false;
+    if (capacity < 0 || (capacity > 0 && (!kinds || !ms)))
+        return fail(KVR_E_ARG, "kinds and ms must hold `capacity` entries");
+    if (n_recorded)
+        *n_recorded = t->n;
+    const int32_t m = t->n < capacity ? t->n : capacity;
+    for (int32_t i = 0; i < m; ++i) {
+        hipError_t e = hipEventSynchronize(t->ev[2 * i + 1]);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms[i], t->ev[2 * i], t->ev[2 * i + 1]);
+        if (e != hipSuccess)
+            return hip_fail(e, "reading launch events");
+        kinds[i] = t->kind[i];
+    }
+    if (t->missed > 0)
+        return fail(KVR_E_CAPACITY, "%d launches ran untimed past the capacity", t->missed);
+    if (m < t->n)
+        return fail(KVR_E_CAPACITY, "%d launches recorded, output holds %d", t->n, capacity);
+    return ok();
 }
 
 }  // extern "C"

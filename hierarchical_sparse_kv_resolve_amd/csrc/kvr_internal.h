@@ -1,8 +1,11 @@
 // Internal declarations of the gfx950 sparse KV row resolver library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "kvr.h"
 
@@ -33,6 +36,17 @@ struct Shape {
     int64_t host_rows;                    // H + max_new
 };
 
+// Launch timing of one context (kvr_timing_begin / kvr_timing_end).
+struct LaunchLog {
+    int32_t cap = 0;            // event pairs created
+    int32_t limit = 0;          // pairs this recording may use
+    int32_t n = 0;              // launches recorded
+    int32_t missed = 0;         // launches past the limit
+    bool on = false;
+    hipEvent_t *ev = nullptr;   // [2 * cap]: start, stop of each launch
+    int32_t *kind = nullptr;    // [cap] kvr_kernel
+};
+
 }  // namespace kvr
 
 struct kvr_ctx {
@@ -52,9 +66,38 @@ struct kvr_ctx {
     kvr::LayerPtrs *layers_d;
     bool *layer_bound;
     size_t resolve_lds;
+    kvr::LaunchLog *timing;  // null until kvr_timing_begin
 };
 
 namespace kvr {
+
+// The next start/stop event pair for a launch of `kind`, when the context is
+// recording and the stream is not being captured.
+bool next_timing_events(const kvr_ctx *c, int32_t kind, hipStream_t s, hipEvent_t *start,
+                        hipEvent_t *stop);
+
+// Every kernel of the library is launched here: plainly, or with the events
+// of a timing recording attached to its dispatch.
+template <typename... P, typename... A>
+hipError_t launch(const kvr_ctx *c, int32_t kind, void (*kernel)(P...), dim3 grid, dim3 block,
+                  size_t lds, hipStream_t s, A... args)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals{static_cast<P>(args)...};
+    void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply([&argv](auto &...v) {
+        int i = 0;
+        ((argv[i++] = static_cast<void *>(&v)), ...);
+    }, vals);
+    hipEvent_t a = nullptr, b = nullptr;
+    const void *fn = reinterpret_cast<const void *>(kernel);
+    hipError_t e = next_timing_events(c, kind, s, &a, &b)
+                       ? hipExtLaunchKernel(fn, grid, block, argv, lds, s, a, b, 0)
+                       : hipLaunchKernel(fn, grid, block, argv, lds, s);
+    if (e != hipSuccess)
+        (void)hipGetLastError();  // the error is returned; do not leave it sticky
+    return e;
+}
 
 // Launchers (return a hipError_t of the launch).
 hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
@@ -86,7 +129,7 @@ hipError_t launch_init_state(const kvr_ctx *c, hipStream_t s);
 hipError_t launch_copy_loc(const kvr_ctx *c, int32_t n, const uint32_t *src, uint32_t *dst,
                            const int32_t *count, int32_t stride, hipStream_t s);
 
-hipError_t launch_dedup(int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
+hipError_t launch_dedup(const kvr_ctx *c, int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
                         int32_t *union_count, int32_t *map, hipStream_t s);
 hipError_t prepare_dedup_kernel();
 

@@ -709,10 +709,12 @@ size_t resolve_lds_bytes(const Shape &sh)
 
 namespace {
 
+using ResolveFn = void (*)(ResolveArgs);
+
 template <int EK, int EB>
-const void *kernel_ptr()
+ResolveFn kernel_ptr()
 {
-    return reinterpret_cast<const void *>(&resolve_kernel<EK, EB>);
+    return &resolve_kernel<EK, EB>;
 }
 
 int per_thread(int n)
@@ -722,7 +724,7 @@ int per_thread(int n)
 }
 
 template <int EK>
-const void *pick_eb(int eb)
+ResolveFn pick_eb(int eb)
 {
     switch (eb) {
     case 1: return kernel_ptr<EK, 1>();
@@ -732,7 +734,7 @@ const void *pick_eb(int eb)
     }
 }
 
-const void *pick_kernel(const Shape &sh)
+ResolveFn pick_kernel(const Shape &sh)
 {
     const int eb = per_thread(sh.B);
     switch (per_thread(sh.sel_cap)) {
@@ -755,7 +757,7 @@ hipError_t prepare_resolve_kernel()
             Shape sh{};
             sh.sel_cap = ek * NT;
             sh.B = eb * NT;
-            hipError_t e = hipFuncSetAttribute(pick_kernel(sh),
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(pick_kernel(sh)),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, most);
             if (e != hipSuccess)
                 return e;
@@ -788,8 +790,7 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
     a.status = status;
     a.stats = stats;
     const size_t lds = resolve_lds_layout(c->shape, &a.vc, &a.hs);
-    void *args[] = {&a};
-    return hipLaunchKernel(pick_kernel(c->shape), dim3(n), dim3(NT), args, lds, s);
+    return launch(c, KVR_KERNEL_RESOLVE, pick_kernel(c->shape), dim3(n), dim3(NT), lds, s, a);
 }
 
 }  // namespace kvr

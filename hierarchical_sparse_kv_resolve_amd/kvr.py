@@ -31,7 +31,10 @@ REUSE_DISTINCT_PAYLOAD = 1
 EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
            "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_gather_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
-           "kvr_host_alloc", "kvr_host_free")
+           "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end")
+
+# kvr_kernel: kinds of the library's kernel launches (launch timing).
+KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state")
 
 
 class KvrError(RuntimeError):
@@ -77,6 +80,8 @@ def lib():
             "kvr_status_summary": [P, I, P],
             "kvr_host_alloc": [U, P],
             "kvr_host_free": [P],
+            "kvr_timing_begin": [P, I],
+            "kvr_timing_end": [P, I, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -194,6 +199,25 @@ class Context:
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
         _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),
                                                  _ptr(union_count), _ptr(map_), _stream(stream)))
+
+    def timing_begin(self, capacity: int):
+        """Record the duration of each kernel this context launches from now on
+        (events on the launches themselves; measurement aid)."""
+        _check(lib().kvr_timing_begin(self.handle, capacity))
+        self._timing_cap = capacity
+
+    def timing_end(self):
+        """Stop recording; waits for the recorded launches.  Returns a list of
+        (kernel name, milliseconds) in launch order."""
+        import numpy as np
+        cap = getattr(self, "_timing_cap", 0)
+        kinds = np.zeros(max(1, cap), dtype=np.int32)
+        ms = np.zeros(max(1, cap), dtype=np.float32)
+        n = ctypes.c_int32()
+        _check(lib().kvr_timing_end(self.handle, cap, kinds.ctypes.data, ms.ctypes.data,
+                                    ctypes.byref(n)))
+        m = min(n.value, cap)
+        return [(KERNEL_NAMES[k], float(t)) for k, t in zip(kinds[:m], ms[:m])]
 
     def reuse_locations(self, mode, dst_layers, n, req_ids, src_loc, dst_loc, count, stride,
                         fills=None, fill_count=None, status=None, stream=None):

@@ -28,21 +28,6 @@ import numpy as np
 from . import kvr
 
 
-class _NoTimer:
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *exc):
-        return False
-
-
-_NO = _NoTimer()
-
-
-def _no_timer(name, stream=None):
-    return _NO
-
-
 class GpuRun:
     def __init__(self, inputs, pool_host=None, device: str = "cuda"):
         import torch
@@ -124,7 +109,7 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, timer=None, prefetch_groups: int = 0, serialize: bool = False):
+    def step(self, s: int, prefetch_groups: int = 0, serialize: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
 
@@ -138,32 +123,27 @@ class GpuRun:
         and several resolving layers, each layer's fill and gather run on the
         side stream while the next layer resolves.
 
-        `timer(name, stream)` may return a context manager that brackets a
-        call with events (used by the benchmark).  serialize=True issues the
-        same launches but lets no two of them overlap, so each call's events
-        time that kernel alone."""
+        serialize=True issues the same launches but lets no two of them
+        overlap, so launch timing (Context.timing_begin) sees each kernel
+        running alone."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
-        tm = timer or _no_timer
         main = torch.cuda.current_stream()
-        with tm("append", main):
-            ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
+        ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
         for g in range(cfg.groups):
             sel = self.sel_dev[s][g]
             k = sel.shape[-1]
             if cfg.q > 1:
-                with tm("dedup", main):
-                    ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
-                                                self.map, stream=main)
+                ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
+                                            self.map, stream=main)
                 src, count, stride = self.union, self.union_count, cfg.q * k
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
             pipelined = prefetch_groups > 0
-            fill_layer = -1 if (timer or pipelined) else 0
-            with tm("resolve", main):
-                ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
-                                 self.status[g], self.stats, stream=main)
+            fill_layer = -1 if pipelined else 0
+            ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
+                             self.status[g], self.stats, stream=main)
             if cfg.reuse != "distinct" and prefetch_groups > 0:
                 # One physical source: this layer's fill and gather run on the
                 # side stream while the main stream resolves the next layer
@@ -174,12 +154,10 @@ class GpuRun:
                 resolved.record(main)
                 side = self._side()
                 side.wait_event(resolved)
-                with tm("refill", side):
-                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
-                                        count, stride, fills, fc, stream=side)
-                with tm("gather", side):
-                    ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
-                                    self.gather_status, stream=side)
+                ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
+                                    count, stride, fills, fc, stream=side)
+                ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
+                                self.gather_status, stream=side)
                 for _ in range(1, cfg.layers_per_group):
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
                                         stride, stream=side)
@@ -189,24 +167,20 @@ class GpuRun:
                     main.wait_event(done)
             elif cfg.reuse != "distinct":
                 if fill_layer < 0:
-                    with tm("refill", main):
-                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
-                                            count, stride, fills, fc, stream=main)
-                with tm("gather", main):
-                    ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
-                                    self.gather_status, stream=main)
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, [0], n, None, loc, None,
+                                        count, stride, fills, fc, stream=main)
+                ctx.gather_rows([0], n, None, loc, count, stride, self.outs[g][:1],
+                                self.gather_status, stream=main)
                 for _ in range(1, cfg.layers_per_group):
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
                                         stride, stream=main)
             elif not pipelined:
                 layers = list(range(1 if fill_layer == 0 else 0, self.nl))
                 if layers:
-                    with tm("refill", main):
-                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, layers, n, None, loc,
-                                            None, count, stride, fills, fc, stream=main)
-                with tm("gather", main):
-                    ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
-                                    self.outs[g], self.gather_status, stream=main)
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, layers, n, None, loc,
+                                        None, count, stride, fills, fc, stream=main)
+                ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
+                                self.outs[g], self.gather_status, stream=main)
             else:
                 groups = np.array_split(np.arange(self.nl), min(prefetch_groups, self.nl))
                 resolved = torch.cuda.Event()
@@ -215,9 +189,8 @@ class GpuRun:
                 side.wait_event(resolved)
                 ready = []
                 for grp in groups:
-                    with tm("refill", side):
-                        ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, grp.tolist(), n, None,
-                                            loc, None, count, stride, fills, fc, stream=side)
+                    ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, grp.tolist(), n, None,
+                                        loc, None, count, stride, fills, fc, stream=side)
                     ev = torch.cuda.Event()
                     ev.record(side)
                     ready.append(ev)
@@ -225,10 +198,9 @@ class GpuRun:
                     ready = [ready[-1]] * len(ready)  # every fill before the first gather
                 for grp, ev in zip(groups, ready):
                     main.wait_event(ev)
-                    with tm("gather", main):
-                        ctx.gather_rows(grp.tolist(), n, None, loc, count, stride,
-                                        [self.outs[g][l] for l in grp], self.gather_status,
-                                        stream=main)
+                    ctx.gather_rows(grp.tolist(), n, None, loc, count, stride,
+                                    [self.outs[g][l] for l in grp], self.gather_status,
+                                    stream=main)
 
     def snapshot(self) -> dict:
         """Device copies of the mutable state (metadata, hot caches, tails)."""

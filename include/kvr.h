@@ -231,6 +231,37 @@ int kvr_status_summary(const int32_t *status, int32_t n, int32_t *first_bad);
 int kvr_host_alloc(size_t bytes, void **out);
 int kvr_host_free(void *ptr);
 
+/* Kernel launch timing (measurement aid, not part of the method).
+ *
+ * Between kvr_timing_begin and kvr_timing_end every kernel the context
+ * launches carries a start and a stop event of its own dispatch
+ * (hipExtLaunchKernel), so each recorded duration is the kernel's execution
+ * alone, the interval a kernel-trace profiler reports, without the gaps
+ * between launches.  Launches on a stream that is being captured into a graph
+ * are not recorded.
+ *
+ * kvr_timing_begin: capacity = most launches to record (1 .. 1048576).
+ *   Creates the events when the context has fewer than that (this is the
+ *   only call here that allocates), then starts recording; launches past the
+ *   capacity run untimed and are counted.
+ * kvr_timing_end: stops recording, waits for the recorded launches and
+ *   writes, for each in launch order, kinds[i] (kvr_kernel) and ms[i] (host
+ *   arrays of `capacity` entries); *n_recorded = launches recorded.  Returns
+ *   KVR_E_CAPACITY if launches went untimed or did not fit the arrays (the
+ *   entries that fit are still written), KVR_E_ARG if recording was not on. */
+typedef enum kvr_kernel {
+    KVR_KERNEL_APPEND = 0,
+    KVR_KERNEL_RESOLVE = 1,
+    KVR_KERNEL_REFILL = 2,   /* host refill and per-layer replays */
+    KVR_KERNEL_GATHER = 3,
+    KVR_KERNEL_DEDUP = 4,
+    KVR_KERNEL_STATE = 5,    /* state initialisation, location copies */
+} kvr_kernel;
+
+int kvr_timing_begin(kvr_ctx *ctx, int32_t capacity);
+int kvr_timing_end(kvr_ctx *ctx, int32_t capacity, int32_t *kinds, float *ms,
+                   int32_t *n_recorded);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,3 +56,15 @@ def test_null_context_and_status_summary():
     assert kvr.status_summary(np.array([0, 0, -2, 0, -3], dtype=np.int32)) == (2, 2)
     assert kvr.status_summary(np.zeros(3, dtype=np.int32)) == (0, -1)
     assert lib.kvr_destroy(None) == kvr.OK
+
+
+def test_kernel_kinds_match_the_binding():
+    text = open(os.path.join(ROOT, "include", "kvr.h")).read()
+    kinds = {name.lower(): int(v) for name, v in re.findall(r"KVR_KERNEL_([A-Z]+)\s*=\s*(\d+)", text)}
+    assert kinds == {name: i for i, name in enumerate(kvr.KERNEL_NAMES)}
+
+
+def test_timing_calls_reject_a_null_context():
+    lib = kvr.lib()
+    assert lib.kvr_timing_begin(None, 8) == kvr.E_ARG
+    assert lib.kvr_timing_end(None, 0, None, None, None) == kvr.E_ARG

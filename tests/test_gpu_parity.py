@@ -375,3 +375,55 @@ def test_graph_replays_match_oracle(shape, prefetch_groups):
             assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l])
     finally:
         gpu.close()
+
+
+@pytest.mark.gpu
+def test_launch_timing_records_each_kernel():
+    """Launch timing records every kernel of a step in launch order with a
+    positive duration, changes no result, records nothing under graph capture
+    and reports launches past its capacity."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2).with_(steps=6)
+    assert cfg.reuse == "distinct" and cfg.payload_layers == 3
+    inputs = Inputs(cfg, max_new=8)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+
+    def compare(o):
+        for g in range(cfg.groups):
+            _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
+        _compare_state(gpu, run, reqs)
+
+    try:
+        gpu.stage(range(cfg.steps))
+        gpu.step(0)
+        compare(run.step(0))
+        gpu.ctx.timing_begin(32)
+        gpu.step(1)
+        rec = gpu.ctx.timing_end()
+        # resolve fills layer 0; one replay call fills layers 1 and 2
+        assert [name for name, _ in rec] == ["append", "resolve", "refill", "refill", "gather"]
+        assert all(0.0 < ms < 1000.0 for _, ms in rec)
+        compare(run.step(1))
+        gpu.ctx.timing_begin(32)
+        gpu.step(2, prefetch_groups=2)
+        rec = gpu.ctx.timing_end()
+        assert [name for name, _ in rec] == ["append", "resolve", "refill", "refill", "gather",
+                                            "gather"]
+        compare(run.step(2))
+        gpu.ctx.timing_begin(32)
+        graph = gpu.capture([3])
+        assert gpu.ctx.timing_end() == []
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(run.step(3))
+        gpu.ctx.timing_begin(2)
+        gpu.step(4)
+        with pytest.raises(kvr.KvrError) as e:
+            gpu.ctx.timing_end()
+        assert e.value.code == kvr.E_CAPACITY
+        compare(run.step(4))
+    finally:
+        gpu.close()
