@@ -47,8 +47,11 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="issue the timed steps eagerly instead of replaying one HIP graph")
-    ap.add_argument("--prefetch-groups", type=int, default=2,
-                    help="layer groups whose host fills overlap earlier gathers (0 = off)")
+    ap.add_argument("--prefetch-groups", default="2",
+                    help="layer groups whose host fills overlap earlier gathers: a count "
+                         "(equal groups, 0 = off) or comma-separated group sizes")
+    ap.add_argument("--hot-slots", type=int, default=0,
+                    help="hot-cache budget B per request (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of known size (for scaling the "
                          "HBM byte counters) and exit")
@@ -236,6 +239,8 @@ def main():
     K, W = args.steps, args.warmup
     total = K + W
     cfg = FULL[c].with_(steps=total)
+    if args.hot_slots:
+        cfg = cfg.with_(B=args.hot_slots)
     inputs = Inputs(cfg, max_new=total)
     log(f"workload {cfg.name}: staging {total} steps")
     gpu = GpuRun(inputs)
@@ -243,6 +248,7 @@ def main():
     log("staged; warming up")
     counts = rows_per_group(inputs, range(W, total))
     pg = args.prefetch_groups
+    pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
     for s in range(W):
         gpu.step(s, prefetch_groups=pg)
     torch.cuda.synchronize()
@@ -319,7 +325,7 @@ def main():
     achieved = bytes_gather / (g_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(cfg.name, pg),
+                "traffic": recorded_traffic(cfg.name, args.prefetch_groups),
                 "kernel": "gather_kernel", "bytes_per_launch": int(bytes_gather),
                 "launch_us": round(g_ms * 1e3, 2),
                 "timing": "start/end events of each gather dispatch (hipExtLaunchKernel) in an "
@@ -371,7 +377,7 @@ def main():
     gpu.close()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
-        line["cpu_baseline"] = cpu_baseline(FULL[c], total, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(cfg, total, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 

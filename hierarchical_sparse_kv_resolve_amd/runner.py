@@ -28,6 +28,17 @@ import numpy as np
 from . import kvr
 
 
+def layer_groups(n_layers: int, prefetch_groups) -> list:
+    """Payload layers split into consecutive groups: G equal groups for an
+    int G, or the given group sizes."""
+    if isinstance(prefetch_groups, int):
+        return np.array_split(np.arange(n_layers), min(prefetch_groups, n_layers))
+    sizes = [int(x) for x in prefetch_groups]
+    if any(x <= 0 for x in sizes) or sum(sizes) != n_layers:
+        raise ValueError(f"group sizes {sizes} do not split {n_layers} layers")
+    return np.split(np.arange(n_layers), np.cumsum(sizes)[:-1])
+
+
 class GpuRun:
     def __init__(self, inputs, pool_host=None, device: str = "cuda"):
         import torch
@@ -109,7 +120,7 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, prefetch_groups: int = 0, serialize: bool = False):
+    def step(self, s: int, prefetch_groups=0, serialize: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
 
@@ -119,7 +130,9 @@ class GpuRun:
         host fills of all layers are issued on a side stream in G groups of
         layers, and each group's gather starts on the current stream as soon
         as that group's fills are in, so host-link traffic of later groups
-        overlaps the HBM traffic of earlier gathers.  With one physical source
+        overlaps the HBM traffic of earlier gathers.  A sequence of group
+        sizes (summing to the layer count) sets the groups explicitly:
+        shrinking groups leave only a small last gather after the last fill.  With one physical source
         and several resolving layers, each layer's fill and gather run on the
         side stream while the next layer resolves.
 
@@ -140,11 +153,11 @@ class GpuRun:
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            pipelined = prefetch_groups > 0
+            pipelined = bool(prefetch_groups)
             fill_layer = -1 if pipelined else 0
             ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
                              self.status[g], self.stats, stream=main)
-            if cfg.reuse != "distinct" and prefetch_groups > 0:
+            if cfg.reuse != "distinct" and pipelined:
                 # One physical source: this layer's fill and gather run on the
                 # side stream while the main stream resolves the next layer
                 # (resolve touches metadata only).  The side stream keeps the
@@ -182,7 +195,7 @@ class GpuRun:
                 ctx.gather_rows(list(range(self.nl)), n, None, loc, count, stride,
                                 self.outs[g], self.gather_status, stream=main)
             else:
-                groups = np.array_split(np.arange(self.nl), min(prefetch_groups, self.nl))
+                groups = layer_groups(self.nl, prefetch_groups)
                 resolved = torch.cuda.Event()
                 resolved.record(main)
                 side = self._side()
@@ -216,7 +229,7 @@ class GpuRun:
         for dst, src in zip(self.tail, snap["tail"]):
             dst.copy_(src)
 
-    def capture(self, steps, prefetch_groups: int = 0):
+    def capture(self, steps, prefetch_groups=0):
         """Capture the launches of `steps` into one HIP graph (nothing runs
         until it is replayed).  Each replay runs those decode steps again from
         whatever state the buffers hold."""
