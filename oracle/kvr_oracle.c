@@ -58,13 +58,13 @@ typedef struct orc_source {
     int32_t n_req, n_layers, H, max_new, P, T, B, R;
     int64_t pool_pages;
     int32_t *L;                 /* [n_req] rows held (imported + decoded)        */
-    const int32_t *page_map;    /* [n_req][n_pages] physical page or -1           */
-    const uint8_t *host_valid;  /* [n_req][n_pages] imported page has host copy   */
+    int32_t *page_map;          /* [n_req][n_pages] physical page or -1           */
+    uint8_t *host_valid;        /* [n_req][n_pages] imported page has host copy   */
     int32_t *tag;               /* [n_req][B] row held by the slot, -1 = empty    */
     uint32_t *stamp;            /* [n_req][B] LRU stamp                           */
     uint32_t *clock;            /* [n_req]    last tick                           */
     uint8_t **tail;             /* per layer [n_req][T][R]                        */
-    uint8_t **pool;             /* per layer [pool_pages][P][R] (read only)       */
+    uint8_t **pool;             /* per layer [pool_pages][P][R]                   */
     uint8_t **hot;              /* per layer [n_req][B][R]                        */
     uint8_t **host;             /* per layer [n_req][H + max_new][R]              */
 } orc_source;
@@ -360,6 +360,84 @@ int orc_dedup_one(int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
     for (int64_t i = 0; i < n; ++i)
         map[i] = find_sorted(union_rows, u, sel[i]);
     return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- residency */
+
+/* Reclamation (section "How it works", paragraph "Reclamation and refill"):
+ * the listed optional pages stop being ready.  A page without a host copy
+ * (resident-first admission deferred its backup) first gets one: its P rows
+ * of every layer are copied from the pool to the host store, so that every
+ * row stays either ready or backed up; only then is the page released.
+ * The list is taken in order.  freed[i] = the physical page released by entry
+ * i, or -1 when that page was not ready (a repeat of an earlier entry
+ * included); status[i] = ORC_E_ARG for a request or page index out of range. */
+void orc_reclaim_pages(orc_source *s, int32_t n, const int32_t *req, const int32_t *page,
+                       int32_t *freed, int32_t *status)
+{
+    const int32_t np = n_pages_of(s);
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t r = req[i], p = page[i];
+        freed[i] = -1;
+        status[i] = ORC_OK;
+        if (r < 0 || r >= s->n_req || p < 0 || p >= np) {
+            status[i] = ORC_E_ARG;
+            continue;
+        }
+        const int32_t phys = s->page_map[(int64_t)r * np + p];
+        if (phys < 0)
+            continue;
+        if (!s->host_valid[(int64_t)r * np + p]) {
+            for (int32_t l = 0; l < s->n_layers; ++l) {
+                uint8_t *dst = s->host[l] + ((int64_t)r * host_rows_of(s) + (int64_t)p * s->P) * s->R;
+                const uint8_t *src = s->pool[l] + (int64_t)phys * s->P * s->R;
+                memcpy(dst, src, (size_t)s->P * s->R);
+            }
+            s->host_valid[(int64_t)r * np + p] = 1;
+        }
+        s->page_map[(int64_t)r * np + p] = -1;
+        freed[i] = phys;
+    }
+}
+
+/* Refill ("Reclamation and refill"): the listed pages become ready again in
+ * the given physical pages: the host rows of every layer are copied into the
+ * pool, then the page map points at them.  The list is taken in order.
+ * status[i]: ORC_E_ARG for a request or page index out of range, a page that
+ * is not complete imported history, or a request/page or physical page that
+ * an earlier entry already names; else ORC_E_RANGE for a physical page outside
+ * the pool; else ORC_E_STATE if the page is already ready; else
+ * ORC_E_NO_HOST_COPY if it has no host copy.  A failed entry changes nothing.
+ * The caller hands out physical pages that no page maps. */
+void orc_restore_pages(orc_source *s, int32_t n, const int32_t *req, const int32_t *page,
+                       const int32_t *phys, int32_t *status)
+{
+    const int32_t np = n_pages_of(s);
+    const int32_t complete = s->H / s->P;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t r = req[i], p = page[i], ph = phys[i];
+        int st = ORC_OK;
+        if (r < 0 || r >= s->n_req || p < 0 || p >= complete)
+            st = ORC_E_ARG;
+        for (int32_t j = 0; j < i && st == ORC_OK; ++j)
+            if ((req[j] == r && page[j] == p) || phys[j] == ph)
+                st = ORC_E_ARG;
+        if (st == ORC_OK && (ph < 0 || (int64_t)ph >= s->pool_pages))
+            st = ORC_E_RANGE;
+        if (st == ORC_OK && s->page_map[(int64_t)r * np + p] >= 0)
+            st = ORC_E_STATE;
+        if (st == ORC_OK && !s->host_valid[(int64_t)r * np + p])
+            st = ORC_E_NO_HOST_COPY;
+        status[i] = st;
+        if (st != ORC_OK)
+            continue;
+        for (int32_t l = 0; l < s->n_layers; ++l) {
+            const uint8_t *src = s->host[l] + ((int64_t)r * host_rows_of(s) + (int64_t)p * s->P) * s->R;
+            uint8_t *dst = s->pool[l] + (int64_t)ph * s->P * s->R;
+            memcpy(dst, src, (size_t)s->P * s->R);
+        }
+        s->page_map[(int64_t)r * np + p] = ph;
+    }
 }
 
 /* ---------------------------------------------------------------- invariants */

@@ -65,6 +65,11 @@ def lib():
             fn = getattr(L, name)
             fn.restype = None
             fn.argtypes = args
+        for name, args in {"orc_reclaim_pages": [P, I, P, P, P, P],
+                           "orc_restore_pages": [P, I, P, P, P, P]}.items():
+            fn = getattr(L, name)
+            fn.restype = None
+            fn.argtypes = args
         L.orc_check_one.restype = ctypes.c_int
         L.orc_check_one.argtypes = [P, I]
         _lib = L
@@ -86,7 +91,7 @@ class OracleSource:
     """One KV source (its metadata and payload layers) as plain numpy arrays.
 
     host[l] must be a private uint8 [n_req][H + max_new][R] array; pool[l] is
-    read only.  All mutable state is owned here.
+    written only by restore_pages.  All mutable state is owned here.
     """
 
     def __init__(self, *, n_req, n_layers, H, max_new, P, T, B, R, page_map, host_valid,
@@ -193,6 +198,30 @@ class OracleSource:
         mp = np.full((n, q, k), -1, dtype=np.int32)
         lib().orc_dedup(self.src, n, q, k, _p(sel), _p(union), _p(ucount), _p(mp), self.threads)
         return union, ucount, mp
+
+    def reclaim_pages(self, req, page):
+        """Release the listed optional pages (backing up those without a host
+        copy).  Returns (freed physical page or -1, status) per entry."""
+        req = np.ascontiguousarray(req, dtype=np.int32)
+        page = np.ascontiguousarray(page, dtype=np.int32)
+        n = len(req)
+        assert page.shape == (n,)
+        freed = np.full(n, -1, dtype=np.int32)
+        status = np.zeros(n, dtype=np.int32)
+        lib().orc_reclaim_pages(self.src, n, _p(req), _p(page), _p(freed), _p(status))
+        return freed, status
+
+    def restore_pages(self, req, page, phys):
+        """Make the listed pages ready in the given physical pages.  Returns
+        the status per entry."""
+        req = np.ascontiguousarray(req, dtype=np.int32)
+        page = np.ascontiguousarray(page, dtype=np.int32)
+        phys = np.ascontiguousarray(phys, dtype=np.int32)
+        n = len(req)
+        assert page.shape == (n,) and phys.shape == (n,)
+        status = np.zeros(n, dtype=np.int32)
+        lib().orc_restore_pages(self.src, n, _p(req), _p(page), _p(phys), _p(status))
+        return status
 
     def check(self) -> np.ndarray:
         """Per request bit mask of violated state invariants (0 = all hold)."""

@@ -1,0 +1,105 @@
+"""Residency policy of the optional pool: the reference.
+
+TEST INFRASTRUCTURE ONLY: tests and the benchmark's scenario checks use it;
+the product path never imports it.  It shares no code with the GPU library's
+policy (a separate C++ implementation).
+
+Follows "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
+Hierarchy", section "How it works":
+  * paragraph "Memory split": complete pages of imported history may sit in
+    reclaimable optional capacity next to the reserve admissions draw from
+    (required + optional + admission reserve within the pool);
+  * paragraph "Reclamation and refill": an admission that leaves a deficit
+    takes whole requests' optional pages, walking the requests in reclaim
+    order, until the deficit is covered; the other requests keep theirs; if
+    the optional pages cannot cover it the admission waits; refill is bounded
+    round-robin.
+
+Readings where the pages are silent:
+  * the reclaim order is the caller's (a list of request ids);
+  * an admission first uses free pages; only the remainder is a deficit, and
+    every ready complete page of a taken request is released, in ascending
+    page order;
+  * physical pages are handed out lowest id first; an admission reserves the
+    lowest free ids and gives them back when it drains;
+  * refill visits requests cyclically from a cursor kept between calls; each
+    visit gives the request its lowest-index complete page that is not
+    ready; it stops after `bound` pages, when no free page is left, or when a
+    whole cycle finds nothing; the cursor then points after the last request
+    served.
+The device side of each decision (host backup of a page without a host copy,
+then release; host rows into the pool, then publish) is orc_reclaim_pages and
+orc_restore_pages in kvr_oracle.c.
+"""
+from __future__ import annotations
+
+import bisect
+
+
+class ResidencyPolicy:
+    def __init__(self, page_map, n_complete: int, pool_pages: int):
+        """page_map: [n_req][n_pages] physical page or -1 (only the first
+        n_complete pages of each request may be optional)."""
+        self.n_req = len(page_map)
+        self.n_complete = int(n_complete)
+        self.ready = [[int(page_map[r][p]) for p in range(self.n_complete)]
+                      for r in range(self.n_req)]
+        used = {ph for row in self.ready for ph in row if ph >= 0}
+        self.free = sorted(set(range(int(pool_pages))) - used)
+        self.reserved = {}
+        self.next_handle = 0
+        self.cursor = 0
+
+    def admit(self, need: int, order):
+        """An admission needing `need` physical pages.  Returns (True, the
+        (request, page) list to reclaim, handle) or (False, [], -1) when the
+        optional pages cannot cover the deficit (nothing changes)."""
+        assert need >= 0
+        deficit = need - len(self.free)
+        plan = []
+        if deficit > 0:
+            for r in order:
+                if deficit <= 0:
+                    break
+                pages = [p for p in range(self.n_complete) if self.ready[r][p] >= 0]
+                plan += [(r, p) for p in pages]
+                deficit -= len(pages)
+            if deficit > 0:
+                return False, [], -1
+            for r, p in plan:
+                bisect.insort(self.free, self.ready[r][p])
+                self.ready[r][p] = -1
+        taken, self.free = self.free[:need], self.free[need:]
+        handle = self.next_handle
+        self.next_handle += 1
+        self.reserved[handle] = taken
+        return True, plan, handle
+
+    def release(self, handle: int) -> None:
+        """The admission drained: its reserved pages are free again."""
+        for ph in self.reserved.pop(handle):
+            bisect.insort(self.free, ph)
+
+    def refill(self, bound: int):
+        """Bounded round-robin refill.  Returns the (request, page, physical
+        page) list to restore."""
+        placed = []
+        idle = 0
+        r = self.cursor
+        while len(placed) < bound and self.free and idle < self.n_req:
+            pages = [p for p in range(self.n_complete) if self.ready[r][p] < 0]
+            if pages:
+                ph = self.free.pop(0)
+                self.ready[r][pages[0]] = ph
+                placed.append((r, pages[0], ph))
+                idle = 0
+                self.cursor = (r + 1) % self.n_req
+            else:
+                idle += 1
+            r = (r + 1) % self.n_req
+        return placed
+
+    def counts(self):
+        """(free pages, ready pages, reserved pages)."""
+        ready = sum(1 for row in self.ready for ph in row if ph >= 0)
+        return len(self.free), ready, sum(len(v) for v in self.reserved.values())

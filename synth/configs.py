@@ -48,6 +48,7 @@ class Workload:
     mix_recent: int = 0          # "mix": window of most recent rows
     mix_recent_frac: float = 0.0  # "mix": share of k drawn from that window
     seed: int = 0
+    pool_spare: int = 0          # optional-pool pages no request holds at admission
 
     @property
     def n_pages(self) -> int:
@@ -65,7 +66,7 @@ class Workload:
 
     @property
     def pool_pages(self) -> int:
-        return self.ready_pages * self.n_req
+        return self.ready_pages * self.n_req + self.pool_spare
 
     @property
     def sel_cap(self) -> int:

@@ -34,6 +34,7 @@ from .configs import Workload
 POISON_HOST = 0xDB      # host rows without a host copy
 POISON_HOT = 0xCD       # hot slots never filled
 POISON_OUT = 0xEE       # gather outputs before the gather
+POISON_FREE_PAGE = 0xFA  # optional-pool pages no request holds
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
@@ -134,8 +135,8 @@ class Inputs:
         page_map = np.full((c.n_req, c.n_pages), -1, dtype=np.int32)
         host_valid = np.ones((c.n_req, c.n_pages), dtype=np.uint8)
         perm = _rng(c.seed, 2).permutation(c.pool_pages).astype(np.int64)
-        owner_req = np.empty(c.pool_pages, dtype=np.int64)
-        owner_page = np.empty(c.pool_pages, dtype=np.int64)
+        owner_req = np.full(c.pool_pages, -1, dtype=np.int64)    # -1: a free page
+        owner_page = np.full(c.pool_pages, -1, dtype=np.int64)
         nxt = 0
         for r in range(c.n_req):
             ready = np.sort(_rng(c.seed, 1, r).choice(c.full_pages, size=c.ready_pages, replace=False))
@@ -180,14 +181,19 @@ class Inputs:
         fill_segments(np.array(segs, dtype=SEG_DTYPE), c.R, self.payload_seed)
 
     def fill_pool(self, layer: int, dst: np.ndarray) -> None:
-        """dst: uint8 [pool_pages][P][R]."""
+        """dst: uint8 [pool_pages][P][R]; free pages get the free-page poison."""
         c = self.cfg
         assert dst.shape == (c.pool_pages, c.P, c.R) and dst.dtype == np.uint8
         assert dst.flags.c_contiguous
         if c.pool_pages == 0:
             return
+        free = self.owner_req < 0
+        if free.any():
+            dst[free] = POISON_FREE_PAGE
         segs = [_seg(dst[ph], c.P, c.R, layer, int(self.owner_req[ph]), int(self.owner_page[ph]) * c.P)
-                for ph in range(c.pool_pages)]
+                for ph in range(c.pool_pages) if self.owner_req[ph] >= 0]
+        if not segs:
+            return
         fill_segments(np.array(segs, dtype=SEG_DTYPE), c.R, self.payload_seed)
 
     def fill_tail(self, layer: int, dst: np.ndarray, reqs=None) -> None:
