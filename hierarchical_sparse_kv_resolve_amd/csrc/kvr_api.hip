@@ -113,6 +113,24 @@ int check_stream(const kvr_ctx *c, hipStream_t s)
 
 }  // namespace
 
+namespace kvr {
+
+int api_fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int api_ok()
+{
+    return ok();
+}
+
+}  // namespace kvr
+
 extern "C" {
 
 const char *kvr_last_error(void) { return g_err; }
@@ -215,7 +233,7 @@ int kvr_destroy(kvr_ctx *ctx)
     return ok();
 }
 
-int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, const int32_t *page_map, const uint8_t *host_valid,
+int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, int32_t *page_map, uint8_t *host_valid,
                       int32_t *tag, uint32_t *stamp, uint32_t *clock)
 {
     if (int rc = check_ctx(ctx, false))
@@ -234,7 +252,7 @@ int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, const int32_t *page_map, const u
     return ok();
 }
 
-int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, const void *pool, void *hot, void *host)
+int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, void *pool, void *hot, void *host)
 {
     if (int rc = check_ctx(ctx, false))
         return rc;
@@ -253,7 +271,7 @@ int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, const void *pool, vo
                     hipGetErrorString(e));
     kvr::LayerPtrs lp;
     lp.tail = static_cast<uint8_t *>(tail);
-    lp.pool = static_cast<const uint8_t *>(pool);
+    lp.pool = static_cast<uint8_t *>(pool);
     lp.hot = static_cast<uint8_t *>(hot);
     lp.host = static_cast<uint8_t *>(host_dev);
     e = hipMemcpy(ctx->layers_d + layer, &lp, sizeof lp, hipMemcpyHostToDevice);
@@ -344,32 +362,29 @@ int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32
         return fail(KVR_E_ARG, "negative stride");
     if (n > 0 && stride > 0 && n_layers > 0 && !loc)
         return fail(KVR_E_ARG, "loc is required");
-    kvr::GatherTarget *targets = nullptr;
-    if (n_layers > 0) {
-        targets = static_cast<kvr::GatherTarget *>(std::malloc(sizeof(kvr::GatherTarget) * n_layers));
-        if (!targets)
-            return fail(KVR_E_ARG, "out of host memory");
-    }
     for (int32_t t = 0; t < n_layers; ++t) {
-        if (int rc = check_layer(ctx, layers[t])) {
-            std::free(targets);
+        if (int rc = check_layer(ctx, layers[t]))
             return rc;
-        }
-        if (!out[t] && n > 0 && stride > 0) {
-            std::free(targets);
+        if (!out[t] && n > 0 && stride > 0)
             return fail(KVR_E_ARG, "out[%d] is null", t);
-        }
-        targets[t].layer = layers[t];
-        targets[t].out = static_cast<uint8_t *>(out[t]);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     int rc = check_stream(ctx, s);
-    if (rc == KVR_OK && n > 0 && stride > 0 && n_layers > 0) {
-        hipError_t e = kvr::launch_gather(ctx, targets, n_layers, n, req_ids, loc, count, stride,
+    // one launch per group of up to kGatherLayersPerLaunch layers
+    kvr::GatherTarget targets[kvr::kGatherLayersPerLaunch];
+    for (int32_t t0 = 0; rc == KVR_OK && n > 0 && stride > 0 && t0 < n_layers;
+         t0 += kvr::kGatherLayersPerLaunch) {
+        const int32_t nt = n_layers - t0 < kvr::kGatherLayersPerLaunch
+                               ? n_layers - t0 : kvr::kGatherLayersPerLaunch;
+        for (int32_t t = 0; t < nt; ++t) {
+            targets[t].layer = layers[t0 + t];
+            targets[t].out = static_cast<uint8_t *>(out[t0 + t]);
+        }
+        hipError_t e = kvr::launch_gather(ctx, targets, nt, n, req_ids, loc, count, stride,
                                           status, s);
-        rc = e == hipSuccess ? KVR_OK : hip_fail(e, "gather launch");
+        if (e != hipSuccess)
+            rc = hip_fail(e, "gather launch");
     }
-    std::free(targets);
     return rc == KVR_OK ? ok() : rc;
 }
 
@@ -436,6 +451,59 @@ int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
             return hip_fail(e, "location copy launch");
     }
     return ok();
+}
+
+// Every payload layer is bound (page moves touch all of them).
+static int check_all_layers(const kvr_ctx *ctx)
+{
+    for (int32_t l = 0; l < ctx->cfg.n_layers; ++l)
+        if (!ctx->layer_bound[l])
+            return fail(KVR_E_ARG, "layer %d not bound", l);
+    return KVR_OK;
+}
+
+static const int32_t kMaxPageList = 65536;
+
+static int check_page_list(const kvr_ctx *ctx, int32_t n, const void *a, const void *b,
+                           const void *c)
+{
+    if (int rc = check_ctx(ctx))
+        return rc;
+    const int64_t most = (int64_t)ctx->cfg.n_req * ctx->shape.n_pages;
+    if (n < 0 || n > most || n > kMaxPageList)
+        return fail(KVR_E_ARG, "page count %d outside [0, min(%lld, %d)]", n, (long long)most,
+                    kMaxPageList);
+    if (n > 0 && (!a || !b || !c))
+        return fail(KVR_E_ARG, "the page lists are required");
+    return check_all_layers(ctx);
+}
+
+int kvr_reclaim_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *pages,
+                      int32_t *freed_phys, int32_t *status, void *stream)
+{
+    if (int rc = check_page_list(ctx, n, req_ids, pages, freed_phys))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    hipError_t e = kvr::launch_reclaim(ctx, n, req_ids, pages, freed_phys, status, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "reclaim launch");
+}
+
+int kvr_restore_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *pages,
+                      const int32_t *phys, int32_t *status, void *stream)
+{
+    if (int rc = check_page_list(ctx, n, req_ids, pages, phys))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    if (n == 0)
+        return ok();
+    hipError_t e = kvr::launch_restore(ctx, n, req_ids, pages, phys, status, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "restore launch");
 }
 
 int kvr_status_summary(const int32_t *status, int32_t n, int32_t *first_bad)

@@ -23,7 +23,7 @@ constexpr uint32_t kIndexMask = 0x3FFFFFFFu;
 // Device-side pointers of one payload layer.
 struct LayerPtrs {
     uint8_t *tail;        // [n_req][T][R]
-    const uint8_t *pool;  // [pool_pages][P][R]
+    uint8_t *pool;        // [pool_pages][P][R]
     uint8_t *hot;         // [n_req][B][R]
     uint8_t *host;        // [n_req][H + max_new][R], device alias of pinned memory
 };
@@ -55,8 +55,8 @@ struct kvr_ctx {
     int device;
     // metadata (device)
     int32_t *L;
-    const int32_t *page_map;
-    const uint8_t *host_valid;
+    int32_t *page_map;
+    uint8_t *host_valid;
     int32_t *tag;
     uint32_t *stamp;
     uint32_t *clock;
@@ -70,6 +70,11 @@ struct kvr_ctx {
 };
 
 namespace kvr {
+
+// Record a message for kvr_last_error() and return `code` / clear it and
+// return KVR_OK (for entry points outside kvr_api.hip).
+int api_fail(int code, const char *fmt, ...);
+int api_ok();
 
 // The next start/stop event pair for a launch of `kind`, when the context is
 // recording and the stream is not being captured.
@@ -132,5 +137,9 @@ hipError_t launch_copy_loc(const kvr_ctx *c, int32_t n, const uint32_t *src, uin
 hipError_t launch_dedup(const kvr_ctx *c, int32_t n, int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
                         int32_t *union_count, int32_t *map, hipStream_t s);
 hipError_t prepare_dedup_kernel();
+hipError_t launch_reclaim(const kvr_ctx *c, int32_t n, const int32_t *req, const int32_t *page,
+                          int32_t *freed, int32_t *status, hipStream_t s);
+hipError_t launch_restore(const kvr_ctx *c, int32_t n, const int32_t *req, const int32_t *page,
+                          const int32_t *phys, int32_t *status, hipStream_t s);
 
 }  // namespace kvr

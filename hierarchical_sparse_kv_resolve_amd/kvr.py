@@ -31,7 +31,10 @@ REUSE_DISTINCT_PAYLOAD = 1
 EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
            "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_gather_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
-           "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end")
+           "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
+           "kvr_reclaim_pages", "kvr_restore_pages", "kvr_residency_create",
+           "kvr_residency_destroy", "kvr_residency_admit", "kvr_residency_release",
+           "kvr_residency_refill", "kvr_residency_counts")
 
 # kvr_kernel: kinds of the library's kernel launches (launch timing).
 KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state")
@@ -82,6 +85,14 @@ def lib():
             "kvr_host_free": [P],
             "kvr_timing_begin": [P, I],
             "kvr_timing_end": [P, I, P, P, P],
+            "kvr_reclaim_pages": [P, I, P, P, P, P, P],
+            "kvr_restore_pages": [P, I, P, P, P, P, P],
+            "kvr_residency_create": [I, I, I, ctypes.c_int64, P, P],
+            "kvr_residency_destroy": [P],
+            "kvr_residency_admit": [P, ctypes.c_int64, I, P, I, P, P, P, P],
+            "kvr_residency_release": [P, I],
+            "kvr_residency_refill": [P, I, I, P, P, P, P],
+            "kvr_residency_counts": [P, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -219,6 +230,14 @@ class Context:
         m = min(n.value, cap)
         return [(KERNEL_NAMES[k], float(t)) for k, t in zip(kinds[:m], ms[:m])]
 
+    def reclaim_pages(self, n, req_ids, pages, freed_phys, status=None, stream=None):
+        _check(lib().kvr_reclaim_pages(self.handle, n, _ptr(req_ids), _ptr(pages),
+                                       _ptr(freed_phys), _ptr(status), _stream(stream)))
+
+    def restore_pages(self, n, req_ids, pages, phys, status=None, stream=None):
+        _check(lib().kvr_restore_pages(self.handle, n, _ptr(req_ids), _ptr(pages), _ptr(phys),
+                                       _ptr(status), _stream(stream)))
+
     def reuse_locations(self, mode, dst_layers, n, req_ids, src_loc, dst_loc, count, stride,
                         fills=None, fill_count=None, status=None, stream=None):
         layers = list(dst_layers or [])
@@ -227,3 +246,71 @@ class Context:
                                          _ptr(src_loc), _ptr(dst_loc), _ptr(count), stride,
                                          _ptr(fills), _ptr(fill_count), _ptr(status),
                                          _stream(stream)))
+
+
+class Residency:
+    """Host-side residency policy of one source's optional pool
+    (kvr_residency_*): which pages to reclaim for an admission and which to
+    refill.  Its decisions are applied with Context.reclaim_pages and
+    Context.restore_pages."""
+
+    def __init__(self, page_map, n_complete: int, pool_pages: int):
+        import numpy as np
+        pm = np.ascontiguousarray(page_map, dtype=np.int32)
+        self.n_req, self.n_pages = pm.shape
+        self.n_complete = int(n_complete)
+        h = ctypes.c_void_p()
+        _check(lib().kvr_residency_create(self.n_req, self.n_pages, self.n_complete,
+                                          int(pool_pages), pm.ctypes.data, ctypes.byref(h)))
+        self.handle = h.value
+
+    def close(self):
+        if self.handle:
+            lib().kvr_residency_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, need: int, order):
+        """(True, [(request, page), ...] to reclaim, handle), or (False, [], -1)
+        when the optional pages cannot cover the deficit."""
+        import numpy as np
+        order = np.ascontiguousarray(order, dtype=np.int32)
+        cap = self.n_req * self.n_complete
+        req = np.zeros(max(1, cap), dtype=np.int32)
+        page = np.zeros(max(1, cap), dtype=np.int32)
+        n, h = ctypes.c_int32(), ctypes.c_int32()
+        rc = lib().kvr_residency_admit(self.handle, int(need), len(order), order.ctypes.data, cap,
+                                       req.ctypes.data, page.ctypes.data, ctypes.byref(n),
+                                       ctypes.byref(h))
+        if rc == E_CAPACITY:
+            return False, [], -1
+        _check(rc)
+        return True, list(zip(req[:n.value].tolist(), page[:n.value].tolist())), h.value
+
+    def release(self, handle: int):
+        _check(lib().kvr_residency_release(self.handle, handle))
+
+    def refill(self, bound: int):
+        """[(request, page, physical page), ...] to restore."""
+        import numpy as np
+        cap = max(1, bound)
+        req = np.zeros(cap, dtype=np.int32)
+        page = np.zeros(cap, dtype=np.int32)
+        phys = np.zeros(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().kvr_residency_refill(self.handle, bound, cap, req.ctypes.data,
+                                          page.ctypes.data, phys.ctypes.data, ctypes.byref(n)))
+        m = n.value
+        return list(zip(req[:m].tolist(), page[:m].tolist(), phys[:m].tolist()))
+
+    def counts(self):
+        """(free pages, ready pages, reserved pages)."""
+        f, r, s = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().kvr_residency_counts(self.handle, ctypes.byref(f), ctypes.byref(r),
+                                          ctypes.byref(s)))
+        return f.value, r.value, s.value

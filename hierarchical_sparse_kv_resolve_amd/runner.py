@@ -215,6 +215,35 @@ class GpuRun:
                                     [self.outs[g][l] for l in grp], self.gather_status,
                                     stream=main)
 
+    # ------------------------------------------------------------------ residency
+    def reclaim_pages(self, plan, stream=None):
+        """Enqueue the release of the (request, page) list `plan` (host backup
+        of pages without one first).  Returns device tensors (freed physical
+        page or -1, status) per entry."""
+        torch = self.torch
+        n = len(plan)
+        req = torch.tensor([r for r, _ in plan] or [0], dtype=torch.int32, device=self.dev)
+        page = torch.tensor([p for _, p in plan] or [0], dtype=torch.int32, device=self.dev)
+        freed = torch.full((max(1, n),), -1, dtype=torch.int32, device=self.dev)
+        status = torch.zeros(max(1, n), dtype=torch.int32, device=self.dev)
+        self.ctx.reclaim_pages(n, req, page, freed, status, stream=stream)
+        return freed[:n], status[:n]
+
+    def restore_pages(self, placed, stream=None):
+        """Enqueue making the (request, page, physical page) list ready.
+        Returns the device status tensor per entry."""
+        torch = self.torch
+        n = len(placed)
+        cols = list(zip(*placed)) if placed else [[0], [0], [0]]
+        req, page, phys = (torch.tensor(list(c), dtype=torch.int32, device=self.dev) for c in cols)
+        status = torch.zeros(max(1, n), dtype=torch.int32, device=self.dev)
+        self.ctx.restore_pages(n, req, page, phys, status, stream=stream)
+        return status[:n]
+
+    def page_state(self) -> dict:
+        self.torch.cuda.synchronize()
+        return {"page_map": self.page_map.cpu().numpy(), "host_valid": self.host_valid.cpu().numpy()}
+
     def snapshot(self) -> dict:
         """Device copies of the mutable state (metadata, hot caches, tails)."""
         return {"L": self.L.clone(), "tag": self.tag.clone(), "stamp": self.stamp.clone(),

@@ -134,15 +134,18 @@ const char *kvr_last_error(void);
  *   host_valid uint8 [n_req][ceil(H/P)]   1 if the imported page has a host copy
  *   tag       int32  [n_req][B]           row held by a hot slot, -1 = empty
  *   stamp     uint32 [n_req][B]           LRU stamp of a hot slot
- *   clock     uint32 [n_req]              last LRU tick of the request */
-int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, const int32_t *page_map, const uint8_t *host_valid,
+ *   clock     uint32 [n_req]              last LRU tick of the request
+ * page_map and host_valid change only in kvr_reclaim_pages and
+ * kvr_restore_pages. */
+int kvr_bind_metadata(kvr_ctx *ctx, int32_t *L, int32_t *page_map, uint8_t *host_valid,
                       int32_t *tag, uint32_t *stamp, uint32_t *clock);
 
 /* Bind one payload layer:
- *   tail (device) [n_req][T][R], pool (device) [pool_pages][P][R] (read only),
+ *   tail (device) [n_req][T][R], pool (device) [pool_pages][P][R] (written
+ *   only by kvr_restore_pages),
  *   hot (device) [n_req][B][R], host (pinned) [n_req][H + max_new][R].
  * tail may be NULL when T = 0 and pool when pool_pages = 0. */
-int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, const void *pool, void *hot,
+int kvr_bind_layer(kvr_ctx *ctx, int32_t layer, void *tail, void *pool, void *hot,
                    void *host);
 
 /* Fresh admission: L = H, every tag -1, every stamp 0, every clock 0. */
@@ -221,6 +224,80 @@ int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
                         uint32_t *dst_loc, const int32_t *count, int32_t stride,
                         const kvr_fill *fills, const int32_t *fill_count, int32_t *status,
                         void *stream);
+
+/* Optional-pool residency ("Adaptive DHiSparse", section "How it works",
+ * paragraph "Reclamation and refill"): every row stays either ready on the
+ * GPU or backed up in host memory, pages are released only after their host
+ * backup and after earlier readers, and released pages are refilled later.
+ *
+ * kvr_reclaim_pages: the listed (req_ids[i], pages[i]) optional pages stop
+ * being ready.  A page without a host copy first gets one (its P rows of
+ * every payload layer are written from the pool to the host store over the
+ * host link), then page_map becomes -1 and host_valid 1.  Stream order makes
+ * the release wait for the kernels enqueued before it (earlier readers), and
+ * every later kernel sees the page released.
+ *   req_ids, pages (device) int32 [n]
+ *   freed_phys (device) int32 [n]: the physical page entry i released, or -1
+ *     if that page was not ready (also for a repeat of an earlier entry)
+ *   status (device) int32 [n] or NULL: KVR_E_ARG for a request or page index
+ *     out of range, KVR_E_STATE for a corrupt map entry (a physical page
+ *     outside the pool, or an incomplete page marked ready; nothing moves),
+ *     else KVR_OK.
+ * kvr_restore_pages: the listed pages become ready in physical pages phys[i]:
+ * their host rows of every layer are copied into the pool, then page_map
+ * points at them.
+ *   req_ids, pages, phys (device) int32 [n]; the caller hands out physical
+ *     pages that no ready page maps (kvr_residency_refill does)
+ *   status (device) int32 [n] or NULL: KVR_E_ARG for a request or page index
+ *     out of range, a page that is not complete imported history, or a page
+ *     or physical page that an earlier entry names; else KVR_E_RANGE for a
+ *     physical page outside the pool; else KVR_E_STATE if the page is ready;
+ *     else KVR_E_NO_HOST_COPY if it has no host copy; a failed entry changes
+ *     nothing.
+ * Both enqueue one kernel on `stream`; n = 0 is a no-op; n is at most
+ * n_req * ceil(H/P). */
+int kvr_reclaim_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *pages,
+                      int32_t *freed_phys, int32_t *status, void *stream);
+int kvr_restore_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *pages,
+                      const int32_t *phys, int32_t *status, void *stream);
+
+/* Host-side residency policy of one KV source's optional pool (no device
+ * work; the caller applies its decisions with the two calls above).
+ *
+ * kvr_residency_create: page_map (host) int32 [n_req][n_pages] the initial
+ *   map, of which the first n_complete pages per request may be optional;
+ *   pool_pages physical pages in the pool, those no page maps are free.
+ * kvr_residency_admit: an admission needing `need` physical pages.  Free
+ *   pages are used first; for the rest (the deficit) whole requests' ready
+ *   pages are taken, walking `order` (n_order request ids, the reclaim
+ *   order), until the deficit is covered; the other requests keep theirs.
+ *   The lowest free page ids are reserved for the admission.  Writes the
+ *   (request, page) list to reclaim, in that order (at most `cap` entries),
+ *   and a handle.  Returns KVR_E_CAPACITY when the optional pages cannot
+ *   cover the deficit (the admission waits; nothing changes, *n_out = 0),
+ *   KVR_E_ARG when the list would exceed `cap` (nothing changes).
+ * kvr_residency_release: the admission drained; its pages are free again.
+ * kvr_residency_refill: bounded round-robin refill: requests are visited
+ *   cyclically from a cursor kept between calls, each visit giving one
+ *   request its lowest-index complete page that is not ready and the lowest
+ *   free physical page, until `bound` pages (at most `cap`), no free page, or
+ *   a whole cycle without an eligible page; the cursor then points after the
+ *   last request served.  Writes (request, page, physical page) triples.
+ * kvr_residency_counts: free, ready and reserved physical pages.
+ * The object is not thread-safe. */
+typedef struct kvr_residency kvr_residency;
+
+int kvr_residency_create(int32_t n_req, int32_t n_pages, int32_t n_complete, int64_t pool_pages,
+                         const int32_t *page_map, kvr_residency **out);
+int kvr_residency_destroy(kvr_residency *res);
+int kvr_residency_admit(kvr_residency *res, int64_t need, int32_t n_order, const int32_t *order,
+                        int32_t cap, int32_t *req_out, int32_t *page_out, int32_t *n_out,
+                        int32_t *handle);
+int kvr_residency_release(kvr_residency *res, int32_t handle);
+int kvr_residency_refill(kvr_residency *res, int32_t bound, int32_t cap, int32_t *req_out,
+                         int32_t *page_out, int32_t *phys_out, int32_t *n_out);
+int kvr_residency_counts(const kvr_residency *res, int64_t *free_pages, int64_t *ready_pages,
+                         int64_t *reserved_pages);
 
 /* Host helper, after the caller has synchronised and copied status to host:
  * number of failed requests; *first_bad = index of the first (or -1). */

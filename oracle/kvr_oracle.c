@@ -371,7 +371,8 @@ int orc_dedup_one(int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
  * row stays either ready or backed up; only then is the page released.
  * The list is taken in order.  freed[i] = the physical page released by entry
  * i, or -1 when that page was not ready (a repeat of an earlier entry
- * included); status[i] = ORC_E_ARG for a request or page index out of range. */
+ * included); status[i] = ORC_E_ARG for a request or page index out of range,
+ * ORC_E_STATE for a map entry outside the pool or on an incomplete page. */
 void orc_reclaim_pages(orc_source *s, int32_t n, const int32_t *req, const int32_t *page,
                        int32_t *freed, int32_t *status)
 {
@@ -387,6 +388,10 @@ void orc_reclaim_pages(orc_source *s, int32_t n, const int32_t *req, const int32
         const int32_t phys = s->page_map[(int64_t)r * np + p];
         if (phys < 0)
             continue;
+        if ((int64_t)phys >= s->pool_pages || p >= s->H / s->P) {
+            status[i] = ORC_E_STATE;  /* a corrupt map entry: nothing moves */
+            continue;
+        }
         if (!s->host_valid[(int64_t)r * np + p]) {
             for (int32_t l = 0; l < s->n_layers; ++l) {
                 uint8_t *dst = s->host[l] + ((int64_t)r * host_rows_of(s) + (int64_t)p * s->P) * s->R;

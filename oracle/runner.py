@@ -43,6 +43,22 @@ class OracleRun:
                                 host_valid=inputs.host_valid[self.reqs], tail=tail, pool=pool,
                                 host=host, threads=threads)
 
+    def _local(self, r):
+        return self.reqs.index(r) if r in self.reqs else -1
+
+    def reclaim_pages(self, plan):
+        """Apply a (request, page) list given in global request ids to the
+        followed requests.  Returns (freed, status) of the applied entries."""
+        keep = [(self._local(r), p) for r, p in plan if self._local(r) >= 0]
+        return self.src.reclaim_pages([r for r, _ in keep], [p for _, p in keep])
+
+    def restore_pages(self, placed):
+        """Apply a (request, page, physical page) list given in global request
+        ids to the followed requests.  Returns the status of applied entries."""
+        keep = [(self._local(r), p, ph) for r, p, ph in placed if self._local(r) >= 0]
+        return self.src.restore_pages([r for r, _, _ in keep], [p for _, p, _ in keep],
+                                      [ph for _, _, ph in keep])
+
     def step(self, s: int, sels=None) -> dict:
         """Run decode step s.  `sels` may supply the per-group selections
         (int32 [n][q][k]); otherwise they come from the generator."""

@@ -49,6 +49,18 @@ def test_reclaim_backs_up_then_releases():
     assert freed[0] == -1 and st[0] == OK
     freed, st = src.reclaim_pages([cfg.n_req, 0], [0, cfg.n_pages])
     assert list(st) == [E_ARG, E_ARG] and list(freed) == [-1, -1]
+    # corrupt map entries (an incomplete page marked ready, a physical page
+    # outside the pool) are refused and nothing moves
+    part = cfg.H // cfg.P
+    assert cfg.H % cfg.P != 0
+    src.page_map[0, part] = 0
+    q = int(np.nonzero(src.page_map[2] >= 0)[0][0])
+    src.page_map[2, q] = cfg.pool_pages
+    host0 = [h.copy() for h in src.host]
+    freed, st = src.reclaim_pages([0, 2], [part, q])
+    assert list(st) == [E_STATE, E_STATE] and list(freed) == [-1, -1]
+    assert src.page_map[0, part] == 0 and src.page_map[2, q] == cfg.pool_pages
+    assert all(np.array_equal(a, b) for a, b in zip(host0, src.host))
 
 
 def test_restore_fills_the_pool_then_publishes():
