@@ -52,6 +52,11 @@ def parse():
                          "(equal groups, 0 = off) or comma-separated group sizes")
     ap.add_argument("--hot-slots", type=int, default=0,
                     help="hot-cache budget B per request (default: the workload's)")
+    ap.add_argument("--scenario", default="", choices=["", "load_step"],
+                    help="load_step: optional-pool residency under an admission that "
+                         "forces reclamation, then its drain and bounded refill")
+    ap.add_argument("--refill-bound", type=int, default=16,
+                    help="load_step: optional pages refilled per decode step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of known size (for scaling the "
                          "HBM byte counters) and exit")
@@ -219,6 +224,125 @@ def zero_copy_read_gbs(torch, gpu, reps=3):
     return best
 
 
+def load_step_scenario(torch, args):
+    """The load-step on/off experiment on the GLM-style shape: a pool with
+    spare pages; after a low-load phase an admission needs the spare pages
+    plus four requests' worth of optional pages (reclaimed whole, in request
+    order, with host backup); it drains after the pressure phase and bounded
+    round-robin refill then repopulates the pool (refill continues into the
+    last phase while free pages and not-ready pages remain).  Reports, per phase, the
+    share of selected rows fetched from host memory and the throughput, and
+    the same steps with no optional residency at all (every page on the host)
+    as the baseline.  The residency plan does not depend on device results, so
+    it is made up front by the library's host policy and its page lists are
+    staged on the device before timing; each step then issues its page moves
+    and its decode step on one stream."""
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    from hierarchical_sparse_kv_resolve_amd.runner import GpuRun
+    from synth import FULL, Inputs, payload_np
+    W, L1, L2, L3, L4 = args.warmup, 12, 16, 112, 16
+    total = W + L1 + L2 + L3 + L4
+    base = FULL[2].with_(steps=total, pool_spare=256)
+    t2, t3 = W + L1 + L2, W + L1 + L2 + L3
+    phases = [("low_load", W, W + L1), ("pressure", W + L1, t2), ("refill", t2, t3),
+              ("after_refill", t3, total)]
+
+    def run_case(cfg, residency):
+        inputs = Inputs(cfg, max_new=total)
+        gpu = GpuRun(inputs)
+        gpu.stage(range(total))
+        plan = {}
+        if residency:
+            pol = kvr.Residency(inputs.page_map, cfg.full_pages, cfg.pool_pages)
+            need = cfg.pool_spare + 4 * cfg.ready_pages - cfg.ready_pages // 2
+            ok, reclaim, handle = pol.admit(need, list(range(cfg.n_req)))
+            assert ok
+            plan[W + L1] = ("reclaim", reclaim)
+            for s in range(W + L1 + L2, total):
+                if s == W + L1 + L2:
+                    pol.release(handle)
+                plan[s] = ("restore", pol.refill(args.refill_bound))
+            pol.close()
+        dev = []  # page lists staged on the device
+        for s in sorted(plan):
+            kind, lst = plan[s]
+            cols = list(zip(*lst)) if lst else []
+            arrs = [torch.tensor(list(c), dtype=torch.int32, device="cuda") for c in cols]
+            n = len(lst)
+            aux = torch.full((max(1, n),), -1, dtype=torch.int32, device="cuda")
+            st = torch.zeros(max(1, n), dtype=torch.int32, device="cuda")
+            plan[s] = (kind, n, arrs, aux, st)
+            dev.append(st)
+        for s in range(W):
+            gpu.step(s, prefetch_groups=2)
+        torch.cuda.synchronize()
+        out = {}
+        moved_bytes = 0
+        for name, lo, hi in phases:
+            before = gpu.stats_dict()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            pages = 0
+            for s in range(lo, hi):
+                if s in plan:
+                    kind, n, arrs, aux, st = plan[s]
+                    if n and kind == "reclaim":
+                        gpu.ctx.reclaim_pages(n, arrs[0], arrs[1], aux, st)
+                    elif n:
+                        gpu.ctx.restore_pages(n, arrs[0], arrs[1], arrs[2], st)
+                    pages += n
+                gpu.step(s, prefetch_groups=2)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            after = gpu.stats_dict()
+            d = {k: after[k] - before[k] for k in after}
+            found = max(1, d["tail"] + d["page"] + d["hit"] + d["miss"])
+            steps = hi - lo
+            rows = steps * cfg.n_req * cfg.k * cfg.payload_layers
+            out[name] = {"steps": steps, "ms_per_step": round(ms / steps, 4),
+                         "rows_per_s": round(rows / (ms * 1e-3), 1),
+                         "host_share": round(d["miss"] / found, 4),
+                         "tail_or_page_share": round((d["tail"] + d["page"]) / found, 4),
+                         "hot_share": round(d["hit"] / found, 4),
+                         "pages_moved": pages,
+                         "page_bytes_per_step": int(pages * cfg.P * cfg.R * cfg.payload_layers
+                                                    / steps)}
+        for st in dev:
+            if (st.cpu().numpy() != 0).any():
+                raise SystemExit("a page move reported an error")
+        for g in range(cfg.groups):
+            if (gpu.status[g].cpu().numpy() != 0).any():
+                raise SystemExit("resolve failed")
+        last = total - 1
+        sel = inputs.selections(last, 0)[:, 0, :]
+        rec = gpu.group(0)
+        for r in range(cfg.n_req):
+            j = np.arange(0, 64)
+            for l, o in enumerate(rec["out"]):
+                if not np.array_equal(o[r, j], payload_np(l, r, sel[r, j], cfg.R, cfg.seed)):
+                    raise SystemExit("gathered bytes differ from the payload closed form")
+        gpu.close()
+        return out
+
+    log("load step: optional residency on")
+    on = run_case(base, True)
+    log("load step: no optional residency (every page on the host)")
+    off = run_case(base.with_(ready_frac=0.0, pool_spare=0), False)
+    line = {"metric": "load-step scenario: host-fetched share of selected rows and rows/s per phase",
+            "scenario": "load_step", "n_gpus": 1, "data": "synthetic", "dtype": "u8",
+            "config": {"workload": base.name, "pool_spare_pages": base.pool_spare,
+                       "ready_pages_per_request": base.ready_pages,
+                       "admission_pages": base.pool_spare + 4 * base.ready_pages
+                       - base.ready_pages // 2,
+                       "refill_bound_pages_per_step": args.refill_bound,
+                       "phases": {name: [lo, hi] for name, lo, hi in phases}},
+            "residency_on": on, "residency_off": off}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -231,6 +355,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.scenario == "load_step":
+        load_step_scenario(torch, args)
         return
     from hierarchical_sparse_kv_resolve_amd.runner import GpuRun
     from synth import FULL, Inputs

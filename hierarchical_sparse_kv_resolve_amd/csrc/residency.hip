@@ -11,8 +11,8 @@
 //
 // Host side: the policy that decides which pages move: an admission covers
 // its deficit with whole requests' ready pages in reclaim order (or waits),
-// and refill hands free physical pages to not-ready pages, bounded, in
-// round-robin over requests.
+// and refill hands free physical pages back to the pages reclamation took,
+// bounded, in round-robin over requests.
 #include <map>
 #include <new>
 #include <set>
@@ -188,6 +188,7 @@ struct kvr_residency {
     std::vector<int32_t> ready;  // [n_req][n_complete]: physical page or -1
     std::set<int32_t> free;      // free physical pages, lowest first
     std::map<int32_t, std::vector<int32_t>> reserved;
+    std::vector<std::set<int32_t>> reclaimed;  // per request: taken, not yet back
     int32_t next_handle = 0;
     int32_t cursor = 0;
 
@@ -216,6 +217,7 @@ int kvr_residency_create(int32_t n_req, int32_t n_pages, int32_t n_complete, int
     std::vector<char> used(pool_pages, 0);
     try {
         res->ready.assign((size_t)n_req * n_complete, -1);
+        res->reclaimed.assign(n_req, std::set<int32_t>());
         for (int32_t r = 0; r < n_req; ++r) {
             for (int32_t p = 0; p < n_complete; ++p) {
                 const int32_t ph = page_map[(int64_t)r * n_pages + p];
@@ -290,6 +292,7 @@ int kvr_residency_admit(kvr_residency *res, int64_t need, int32_t n_order, const
                 continue;
             res->free.insert(ph);
             ph = -1;
+            res->reclaimed[r].insert(p);
             req_out[k] = r;
             page_out[k] = p;
             ++k;
@@ -331,10 +334,10 @@ int kvr_residency_refill(kvr_residency *res, int32_t bound, int32_t cap, int32_t
     const int32_t limit = bound < cap ? bound : cap;
     int32_t k = 0, idle = 0, r = res->cursor;
     while (k < limit && !res->free.empty() && idle < res->n_req) {
-        int32_t p = 0;
-        while (p < res->n_complete && res->at(r, p) >= 0)
-            ++p;
-        if (p < res->n_complete) {
+        std::set<int32_t> &back = res->reclaimed[r];
+        if (!back.empty()) {
+            const int32_t p = *back.begin();
+            back.erase(back.begin());
             const int32_t ph = *res->free.begin();
             res->free.erase(res->free.begin());
             res->at(r, p) = ph;

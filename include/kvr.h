@@ -277,12 +277,14 @@ int kvr_restore_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int
  *   cover the deficit (the admission waits; nothing changes, *n_out = 0),
  *   KVR_E_ARG when the list would exceed `cap` (nothing changes).
  * kvr_residency_release: the admission drained; its pages are free again.
- * kvr_residency_refill: bounded round-robin refill: requests are visited
- *   cyclically from a cursor kept between calls, each visit giving one
- *   request its lowest-index complete page that is not ready and the lowest
+ * kvr_residency_refill: bounded round-robin refill of the pages that
+ *   reclamation took (residency repopulates as load drains): requests are
+ *   visited cyclically from a cursor kept between calls, each visit giving
+ *   one request its lowest-index reclaimed page not yet back and the lowest
  *   free physical page, until `bound` pages (at most `cap`), no free page, or
- *   a whole cycle without an eligible page; the cursor then points after the
- *   last request served.  Writes (request, page, physical page) triples.
+ *   a whole cycle without such a page; the cursor then points after the last
+ *   request served.  Pages not ready at creation are never refilled.  Writes
+ *   (request, page, physical page) triples.
  * kvr_residency_counts: free, ready and reserved physical pages.
  * The object is not thread-safe. */
 typedef struct kvr_residency kvr_residency;

@@ -22,10 +22,13 @@ Readings where the pages are silent:
     page order;
   * physical pages are handed out lowest id first; an admission reserves the
     lowest free ids and gives them back when it drains;
+  * refill brings back the pages reclamation took (the evidence section's
+    load-step experiment: residency "repopulates as requests drain"); pages
+    that were not ready at admission stay as admission left them;
   * refill visits requests cyclically from a cursor kept between calls; each
-    visit gives the request its lowest-index complete page that is not
-    ready; it stops after `bound` pages, when no free page is left, or when a
-    whole cycle finds nothing; the cursor then points after the last request
+    visit gives the request its lowest-index reclaimed page not yet back; it
+    stops after `bound` pages, when no free page is left, or when a whole
+    cycle finds nothing; the cursor then points after the last request
     served.
 The device side of each decision (host backup of a page without a host copy,
 then release; host rows into the pool, then publish) is orc_reclaim_pages and
@@ -46,6 +49,7 @@ class ResidencyPolicy:
                       for r in range(self.n_req)]
         used = {ph for row in self.ready for ph in row if ph >= 0}
         self.free = sorted(set(range(int(pool_pages))) - used)
+        self.taken = [[] for _ in range(self.n_req)]  # reclaimed, not yet back
         self.reserved = {}
         self.next_handle = 0
         self.cursor = 0
@@ -69,10 +73,11 @@ class ResidencyPolicy:
             for r, p in plan:
                 bisect.insort(self.free, self.ready[r][p])
                 self.ready[r][p] = -1
-        taken, self.free = self.free[:need], self.free[need:]
+                bisect.insort(self.taken[r], p)
+        mine, self.free = self.free[:need], self.free[need:]
         handle = self.next_handle
         self.next_handle += 1
-        self.reserved[handle] = taken
+        self.reserved[handle] = mine
         return True, plan, handle
 
     def release(self, handle: int) -> None:
@@ -81,17 +86,17 @@ class ResidencyPolicy:
             bisect.insort(self.free, ph)
 
     def refill(self, bound: int):
-        """Bounded round-robin refill.  Returns the (request, page, physical
-        page) list to restore."""
+        """Bounded round-robin refill of reclaimed pages.  Returns the
+        (request, page, physical page) list to restore."""
         placed = []
         idle = 0
         r = self.cursor
         while len(placed) < bound and self.free and idle < self.n_req:
-            pages = [p for p in range(self.n_complete) if self.ready[r][p] < 0]
-            if pages:
+            if self.taken[r]:
+                p = self.taken[r].pop(0)
                 ph = self.free.pop(0)
-                self.ready[r][pages[0]] = ph
-                placed.append((r, pages[0], ph))
+                self.ready[r][p] = ph
+                placed.append((r, p, ph))
                 idle = 0
                 self.cursor = (r + 1) % self.n_req
             else:

@@ -134,27 +134,34 @@ def test_policy_hand_worked():
     # needs 3: free pages cover it; the lowest free ids are reserved
     ok, plan, h0 = pol.admit(3, [0, 1, 2])
     assert ok and plan == [] and pol.reserved[h0] == [4, 6, 8] and pol.free == [9]
-    # needs 4 with 1 free: deficit 3; request 0 (3 pages) covers it, request 2
-    # keeps its pages; request 1 has none; order 1, 0, 2
+    # needs 4 with 1 free: deficit 3; request 1 has no ready page, request 0
+    # (3 pages) covers it, request 2 keeps its pages
     ok, plan, h1 = pol.admit(4, [1, 0, 2])
     assert ok and plan == [(0, 0), (0, 2), (0, 3)]
     assert pol.reserved[h1] == [0, 3, 7, 9] and pol.free == []
     # needs 5 with 0 free: request 2's 3 pages cannot cover it: wait
     ok, plan, h2 = pol.admit(5, [0, 1, 2])
     assert not ok and plan == [] and h2 == -1 and pol.counts() == (0, 3, 7)
-    # the first admission drains; refill 2 pages round-robin from request 0
+    # the first admission drains; refill brings request 0's pages back, 2 now
     pol.release(h0)
     assert pol.free == [4, 6, 8]
-    assert pol.refill(2) == [(0, 0, 4), (1, 0, 6)]
-    assert pol.cursor == 2
-    # request 2's only not-ready page is 2; then back to request 0
-    assert pol.refill(5) == [(2, 2, 8)]
-    assert pol.cursor == 0 and pol.free == []
+    assert pol.refill(2) == [(0, 0, 4), (0, 2, 6)]
+    assert pol.cursor == 1
+    assert pol.refill(5) == [(0, 3, 8)]
+    assert pol.cursor == 1 and pol.free == []
+    # page 1 of request 0 and all of request 1 were never ready: not refilled
     pol.release(h1)
-    # request 0 holds page 0 again; its lowest page not ready is 1 (never
-    # ready at admission); request 1 gets its page 1; request 2 is complete
-    assert pol.refill(3) == [(0, 1, 0), (1, 1, 3), (0, 2, 7)]
-    assert pol.counts() == (1, 10 - 1, 0)
+    assert pol.refill(3) == [] and pol.free == [0, 3, 7, 9]
+    # needs 8 with 4 free: deficit 4: request 2 (3 pages), then request 0
+    ok, plan, h3 = pol.admit(8, [2, 0])
+    assert ok and plan == [(2, 0), (2, 1), (2, 3), (0, 0), (0, 2), (0, 3)]
+    assert pol.reserved[h3] == list(range(8)) and pol.free == [8, 9]
+    pol.release(h3)
+    # round robin from the cursor (request 1, nothing to bring back):
+    # request 2, request 0, request 2, request 0
+    assert pol.refill(4) == [(2, 0, 0), (0, 0, 1), (2, 1, 2), (0, 2, 3)]
+    assert pol.cursor == 1
+    assert pol.counts() == (6, 4, 0)
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -172,6 +179,7 @@ def test_policy_properties(seed):
                 k += 1
     pol = ResidencyPolicy(pm, n_complete, pool)
     handles = []
+    back = [set() for _ in range(n_req)]  # reclaimed pages not yet refilled
     for _ in range(30):
         free0 = list(pol.free)
         ready0 = [list(row) for row in pol.ready]
@@ -198,39 +206,42 @@ def test_policy_properties(seed):
                 got = sum(ready_of[r] for r in taken)
                 assert got >= deficit and got - ready_of[taken[-1]] < deficit
                 assert plan == [(r, p) for r in taken for p in range(n_complete) if ready0[r][p] >= 0]
+            for r, p in plan:
+                back[r].add(p)
             handles.append(h)
             pool_after = sorted(free0 + [ready0[r][p] for r, p in plan])
             assert pol.reserved[h] == pool_after[:need] and pol.free == pool_after[need:]
         elif op == 1 and handles:
             h = handles.pop(int(rng.integers(0, len(handles))))
-            back = pol.reserved[h]
+            returned = pol.reserved[h]
             pol.release(h)
-            assert pol.free == sorted(free0 + back)
+            assert pol.free == sorted(free0 + returned)
         else:
             bound = int(rng.integers(0, 6))
             cur = pol.cursor
             placed = pol.refill(bound)
             assert len(placed) <= bound
             assert [ph for _, _, ph in placed] == free0[:len(placed)]
-            eligible = [r for r in range(n_req) if any(ph < 0 for ph in ready0[r])]
+            # only reclaimed pages come back, each request's lowest first
             served = [r for r, _, _ in placed]
-            # each page: the request's lowest not-ready page at that moment
-            seen = {}
-            for r, p, _ in placed:
-                lows = [q for q in range(n_complete) if ready0[r][q] < 0]
-                assert p == lows[seen.get(r, 0)]
-                seen[r] = seen.get(r, 0) + 1
-            # round robin from the cursor: no request is served twice before
-            # every eligible request still holding a not-ready page was served once
-            counts = [served.count(r) for r in range(n_req)]
+            for r in range(n_req):
+                got = [p for rr, p, _ in placed if rr == r]
+                assert got == sorted(back[r])[:len(got)]
+                back[r] -= set(got)
+            eligible = [r for r in range(n_req) if any(rr == r for rr, _, _ in placed)
+                        or back[r]]
+            # round robin from the cursor: the first served request is the
+            # first eligible one from the cursor; counts differ by at most one
+            # among requests that still had pages to bring back
             if served:
                 assert served[0] == next(r for r in [(cur + i) % n_req for i in range(n_req)]
                                          if r in eligible)
-                assert max(counts) - min(counts[r] for r in eligible
-                                         if sum(ph < 0 for ph in ready0[r]) > counts[r]
-                                         or counts[r] == max(counts)) <= 1
+                counts = [served.count(r) for r in range(n_req)]
+                still = [r for r in eligible if back[r]]
+                if still:
+                    assert max(counts) - min(counts[r] for r in still) <= 1
             if len(placed) < bound:
-                assert not pol.free or all(ph >= 0 for row in pol.ready for ph in row)
+                assert not pol.free or not any(back)
         f, rd, rs = pol.counts()
         assert f + rd + rs == pool
         used = [ph for row in pol.ready for ph in row if ph >= 0]

@@ -78,7 +78,7 @@ def test_library_policy_rejects_bad_arguments():
         assert ok and plan == [(1, 1), (0, 0), (0, 2)]
         assert pol.counts() == (1, 0, 3)
         pol.release(h)
-        assert pol.refill(2) == [(0, 0, 0), (1, 0, 1)]
+        assert pol.refill(2) == [(0, 0, 0), (1, 1, 1)]  # the reclaimed pages come back
     finally:
         pol.close()
     lib = kvr.lib()
