@@ -32,8 +32,10 @@
  *
  * Location word: bits 31..30 hold the place (0 tail, 1 optional page, 2 hot
  * cache, 3 invalid) and bits 29..0 the index there (ring slot, global pool row
- * = physical page * P + offset, or hot slot).  0xFFFFFFFF marks a row of a
- * failed request.
+ * = physical page * P + offset, or hot slot).  In a hot-cache word bit 29 is
+ * the fresh flag: the row was copied from host memory by this call (a
+ * consumer can take those bytes as they arrive); bits 28..0 are the slot.
+ * 0xFFFFFFFF marks a row of a failed request.
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -50,6 +52,7 @@ enum {
 };
 
 #define ORC_INVALID 0xFFFFFFFFu
+#define ORC_FRESH (1u << 29) /* hot-cache word: the row was copied from host in this call */
 
 /* statistics slots, added to by every call */
 enum { ST_CALLS, ST_TAIL, ST_PAGE, ST_HIT, ST_MISS, ST_FILL, ST_HOST_BYTES, ST_ERROR, ST_N };
@@ -277,12 +280,13 @@ int orc_resolve_one(const orc_source *s, int32_t r, const int32_t *sel, int32_t 
             stats[ST_PAGE] += 1;
         } else {
             int32_t i = find_sorted(U, nU, pos);
-            loc[j] = (2u << 30) | (uint32_t)slot_of[i];
             /* a row is a hit if its slot was already holding it before this call */
             int filled_now = 0;
             for (int32_t f = 0; f < m; ++f)
                 if (fills[2 * f] == pos)
                     filled_now = 1;
+            /* a row copied from host in this call carries the fresh flag */
+            loc[j] = (2u << 30) | (filled_now ? ORC_FRESH : 0u) | (uint32_t)slot_of[i];
             stats[filled_now ? ST_MISS : ST_HIT] += 1;
         }
     }
@@ -330,8 +334,8 @@ int orc_gather_one(const orc_source *s, int32_t layer, int32_t r, const uint32_t
             src = s->tail[layer] + ((int64_t)r * s->T + idx) * s->R;
         else if (place == 1 && (int64_t)idx < s->pool_pages * s->P)
             src = s->pool[layer] + (int64_t)idx * s->R;
-        else if (place == 2 && idx < (uint32_t)s->B)
-            src = s->hot[layer] + ((int64_t)r * s->B + idx) * s->R;
+        else if (place == 2 && (idx & ~ORC_FRESH) < (uint32_t)s->B)
+            src = s->hot[layer] + ((int64_t)r * s->B + (idx & ~ORC_FRESH)) * s->R;
         if (!src) {
             status = ORC_E_RANGE;
             continue;

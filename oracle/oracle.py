@@ -24,6 +24,7 @@ E_NO_HOST_COPY = -4
 E_STATE = -6
 
 INVALID = 0xFFFFFFFF
+FRESH = 1 << 29  # hot-cache location word: copied from host in this call
 STAT_NAMES = ("calls", "tail", "page", "hit", "miss", "fill", "host_bytes", "error")
 
 _P = ctypes.c_void_p

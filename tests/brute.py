@@ -11,6 +11,7 @@ the same readings of what the statement leaves open.
 from __future__ import annotations
 
 OK, E_RANGE, E_CAPACITY, E_NO_HOST_COPY = 0, -2, -3, -4
+FRESH = 1 << 29  # hot-cache location: the row was copied from host in this call
 
 
 class BruteSource:
@@ -80,7 +81,9 @@ class BruteSource:
                 pg = p // self.P
                 loc.append((1, self.page_map[pg] * self.P + p % self.P))
             else:
-                loc.append((2, place[p]))
+                # rows copied from host in this call carry the fresh flag
+                fresh = FRESH if p in misses else 0
+                loc.append((2, place[p] | fresh))
         return OK, loc, fills
 
     def replay(self, layer, fills):
@@ -92,7 +95,7 @@ class BruteSource:
         if place == 0:
             return self.tail[layer][index]
         if place == 2:
-            return self.hot[layer][index]
+            return self.hot[layer][index & ~FRESH]
         phys, off = divmod(index, self.P)
         return self.page_map.index(phys) * self.P + off
 

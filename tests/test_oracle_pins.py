@@ -28,6 +28,9 @@ from tests.helpers import new_row, one_request_source
 TAIL, PAGE, HOT = 0, 1, 2
 
 
+FRESH = 1 << 29  # hot-cache word of a row copied from host in the call
+
+
 def word(place, idx):
     return (place << 30) | idx
 
@@ -72,6 +75,7 @@ def test_hand_worked_trace():
       call 5: row 9 >= L -> range error, nothing changes
       call 6: 6 misses; least recent is slot 1 (stamp 2) -> tags [4,6],
               stamps [3,4], clock 4
+    Hot-cache words of rows copied from host in the call carry the fresh flag.
     """
     src = one_request_source(H=8, P=4, T=2, B=2, page_map=[3, -1], host_valid=[0, 1])
 
@@ -80,18 +84,19 @@ def test_hand_worked_trace():
 
     loc, fills, fc, st = call([5, 1, 7, 4])
     assert st[0] == orc.OK
-    assert loc[0].tolist() == [word(HOT, 1), word(PAGE, 13), word(TAIL, 1), word(HOT, 0)]
+    assert loc[0].tolist() == [word(HOT, 1) | FRESH, word(PAGE, 13), word(TAIL, 1),
+                               word(HOT, 0) | FRESH]
     assert fills[0, :fc[0]].tolist() == [[4, 0], [5, 1]]
     assert src.tag[0].tolist() == [4, 5] and src.stamp[0].tolist() == [1, 1] and src.clock[0] == 1
 
     assert src.append(new_row(src, 8))[0] == orc.OK and src.L[0] == 9
     loc, fills, fc, st = call([6, 5])
-    assert loc[0].tolist() == [word(HOT, 0), word(HOT, 1)]
+    assert loc[0].tolist() == [word(HOT, 0) | FRESH, word(HOT, 1)]
     assert fills[0, :fc[0]].tolist() == [[6, 0]]
     assert src.tag[0].tolist() == [6, 5] and src.stamp[0].tolist() == [2, 2]
 
     loc, fills, fc, st = call([4, 8, 2])
-    assert loc[0].tolist() == [word(HOT, 0), word(TAIL, 0), word(PAGE, 14)]
+    assert loc[0].tolist() == [word(HOT, 0) | FRESH, word(TAIL, 0), word(PAGE, 14)]
     assert src.tag[0].tolist() == [4, 5] and src.stamp[0].tolist() == [3, 2] and src.clock[0] == 3
 
     loc, fills, fc, st = call([6, 5, 4])
@@ -102,12 +107,13 @@ def test_hand_worked_trace():
     assert st[0] == orc.E_RANGE and (loc == orc.INVALID).all() and src.clock[0] == 3
 
     loc, fills, fc, st = call([6])
-    assert loc[0].tolist() == [word(HOT, 1)]
+    assert loc[0].tolist() == [word(HOT, 1) | FRESH]
     assert src.tag[0].tolist() == [4, 6] and src.stamp[0].tolist() == [3, 4] and src.clock[0] == 4
 
-    # the hot cache now holds the host bytes of rows 4 and 6, the gather finds them
-    out, gst = src.gather(0, np.array([[word(HOT, 0), word(HOT, 1), word(PAGE, 13), word(TAIL, 0)]],
-                                      dtype=np.uint32))
+    # the hot cache now holds the host bytes of rows 4 and 6, the gather finds
+    # them (with or without the fresh flag)
+    out, gst = src.gather(0, np.array([[word(HOT, 0), word(HOT, 1) | FRESH, word(PAGE, 13),
+                                        word(TAIL, 0)]], dtype=np.uint32))
     assert gst[0] == orc.OK
     assert np.array_equal(out[0], payload_np(0, 0, np.array([4, 6, 1, 8]), src.R, 7))
 
@@ -200,7 +206,7 @@ def test_single_row_calls_are_textbook_lru(B):
             lru[u] = True
         assert (fc[0] == 0) == hit
         assert set(t for t in src.tag[0].tolist() if t >= 0) == set(lru)
-        assert src.tag[0][loc[0, 0] & 0x3FFFFFFF] == u
+        assert src.tag[0][loc[0, 0] & (FRESH - 1)] == u
 
 
 # ----------------------------------------------------------------- special cases
@@ -364,7 +370,7 @@ def test_reduced_workload_invariants_and_bytes(c):
                 assert np.array_equal(place, expect)
                 # hit slots are not victims; all referenced slots carry the new tick
                 fslots = rec["fills"][r, : rec["fill_count"][r], 1]
-                hot_slots = np.unique(loc[place == 2] & 0x3FFFFFFF)
+                hot_slots = np.unique(loc[place == 2] & (FRESH - 1))
                 hit_slots = np.setdiff1d(hot_slots, fslots)
                 tick = src.clock[r] - (cfg.groups - 1 - g)   # this group's tick
                 if g == cfg.groups - 1:
