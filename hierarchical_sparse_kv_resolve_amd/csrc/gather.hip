@@ -5,6 +5,17 @@
 // that location word j of request i names in that layer's tail, optional
 // pool or hot cache.  One launch serves every payload layer that shares the
 // location vector (grid z = layer).
+//
+// Three modes of one kernel:
+//   all       every valid word (fresh hot-cache rows read from their slots);
+//   resident  every valid word except fresh hot-cache rows; it reads no slot
+//             a fill of the same call writes, so it runs beside the fills;
+//   fill      only fresh hot-cache rows: each is read once from the layer's
+//             pinned host store (its row is the selection entry's) and
+//             written both to the slot (the host fill of step 3 of
+//             "Resolution") and to the output, one pass over the host link
+//             for both.  It reads the selection, not the tags, so a later
+//             resolve of the same requests may already be rewriting tags.
 #include "kvr_internal.h"
 #include "rows.h"
 
@@ -22,13 +33,40 @@ struct GatherArgs {
     const int32_t *req_ids;
     const uint32_t *loc;
     const int32_t *count;
+    const int32_t *sel;       // [n][stride] the resolved selection (fill mode)
     int32_t stride;
     int32_t *status;
 };
 
+// Source of a word in the all and resident modes (null: nothing to copy).
+__device__ __forceinline__ const uint8_t *resident_src(const GatherArgs &a, const LayerPtrs &lp,
+                                                       int r, uint32_t w, bool skip_fresh,
+                                                       bool &bad)
+{
+    bad = false;
+    if (w == KVR_LOC_INVALID)
+        return nullptr;
+    const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
+    if (place == KVR_PLACE_TAIL && idx < (uint32_t)a.sh.T)
+        return lp.tail + ((int64_t)r * a.sh.T + idx) * a.sh.R;
+    if (place == KVR_PLACE_PAGE && (int64_t)idx < a.sh.pool_rows)
+        return lp.pool + (int64_t)idx * a.sh.R;
+    if (place == KVR_PLACE_HOT && (idx & kSlotMask) < (uint32_t)a.sh.B) {
+        if (skip_fresh && (idx & kFreshBit))
+            return nullptr;
+        return lp.hot + ((int64_t)r * a.sh.B + (idx & kSlotMask)) * a.sh.R;
+    }
+    bad = true;
+    return nullptr;
+}
+
+template <int MODE>
 __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 {
     __shared__ const uint8_t *sSrc[kMaxTileRows];
+    __shared__ uint8_t *sOut[kMaxTileRows];  // fill mode
+    __shared__ uint8_t *sHot[kMaxTileRows];  // fill mode
+    __shared__ int sRows;
     const int i = blockIdx.y;
     const int t = blockIdx.z;
     const int r = a.req_ids ? a.req_ids[i] : i;
@@ -40,56 +78,84 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
     const int nrows = min(a.ts.rows, cnt - j0);
     const LayerPtrs lp = a.layers[a.layer[t]];
     const int R = a.sh.R;
-    if ((int)threadIdx.x < nrows) {
-        const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
-        const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
-        const uint8_t *src = nullptr;
-        if (w != KVR_LOC_INVALID) {
-            if (place == KVR_PLACE_TAIL && idx < (uint32_t)a.sh.T)
-                src = lp.tail + ((int64_t)r * a.sh.T + idx) * R;
-            else if (place == KVR_PLACE_PAGE && (int64_t)idx < a.sh.pool_rows)
-                src = lp.pool + (int64_t)idx * R;
-            else if (place == KVR_PLACE_HOT && idx < (uint32_t)a.sh.B)
-                src = lp.hot + ((int64_t)r * a.sh.B + idx) * R;
-            else if (a.status)
+    uint8_t *dst = a.out[t] + ((int64_t)i * a.stride + j0) * R;
+    int rows = nrows;
+    if (MODE == kGatherFill) {
+        // compact this tile's fresh rows (their order does not matter: each
+        // has its own destinations)
+        if (threadIdx.x == 0)
+            sRows = 0;
+        __syncthreads();
+        if ((int)threadIdx.x < nrows) {
+            const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
+            const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
+            if (w != KVR_LOC_INVALID && place == KVR_PLACE_HOT && (idx & kFreshBit)) {
+                const uint32_t slot = idx & kSlotMask;
+                const int32_t row = a.sel[(int64_t)i * a.stride + j0 + threadIdx.x];
+                if (slot < (uint32_t)a.sh.B && row >= 0 && (int64_t)row < a.sh.host_rows) {
+                    const int k = atomicAdd(&sRows, 1);
+                    sSrc[k] = lp.host + ((int64_t)r * a.sh.host_rows + row) * R;
+                    sHot[k] = lp.hot + ((int64_t)r * a.sh.B + slot) * R;
+                    sOut[k] = dst + (int64_t)threadIdx.x * R;
+                } else if (a.status) {
+                    a.status[i] = KVR_E_RANGE;
+                }
+            }
+        }
+        __syncthreads();
+        rows = sRows;
+        if (rows == 0)
+            return;
+    } else {
+        if ((int)threadIdx.x < nrows) {
+            const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
+            bool bad;
+            sSrc[threadIdx.x] = resident_src(a, lp, r, w, MODE == kGatherResident, bad);
+            if (bad && a.status)
                 a.status[i] = KVR_E_RANGE;
         }
-        sSrc[threadIdx.x] = src;
+        __syncthreads();
     }
-    __syncthreads();
-    uint8_t *dst = a.out[t] + ((int64_t)i * a.stride + j0) * R;
     const int C = a.ts.chunks;
-    const int total = nrows * C;
+    const int total = rows * C;
     for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
         u32x4 v[kUnroll];
-        const uint8_t *srcs[kUnroll];
+        int rr[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int c = c0 + u * NT + threadIdx.x;
-            srcs[u] = nullptr;
+            rr[u] = -1;
             if (c < total) {
                 const int row = (int)(((uint64_t)(uint32_t)c * a.ts.magic) >> 32);
                 const uint8_t *s = sSrc[row];
                 if (s) {
-                    srcs[u] = s;
+                    rr[u] = row;
                     load_chunk(v[u], s + (c - row * C) * 16);
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            if (rr[u] < 0)
+                continue;
             const int c = c0 + u * NT + threadIdx.x;
-            if (srcs[u])
+            if (MODE == kGatherFill) {
+                const int off = (c - rr[u] * C) * 16;
+                store_chunk(sHot[rr[u]] + off, v[u]);
+                store_chunk_nt(sOut[rr[u]] + off, v[u]);
+            } else {
                 store_chunk_nt(dst + (int64_t)c * 16, v[u]);
+            }
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t n_targets,
-                         int32_t n, const int32_t *req_ids, const uint32_t *loc,
-                         const int32_t *count, int32_t stride, int32_t *status, hipStream_t s)
+hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *targets,
+                         int32_t n_targets, int32_t n, const int32_t *req_ids, const uint32_t *loc,
+                         const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,
+                         hipStream_t s)
 {
     GatherArgs a;
     a.sh = c->shape;
@@ -98,6 +164,7 @@ hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t 
     a.req_ids = req_ids;
     a.loc = loc;
     a.count = count;
+    a.sel = sel;
     a.stride = stride;
     a.status = status;
     for (int32_t t0 = 0; t0 < n_targets; t0 += kGatherLayersPerLaunch) {
@@ -107,7 +174,13 @@ hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t 
             a.out[t] = targets[t0 + t].out;
         }
         dim3 grid((stride + a.ts.rows - 1) / a.ts.rows, n, nt);
-        hipError_t e = launch(c, KVR_KERNEL_GATHER, gather_kernel, grid, dim3(NT), 0, s, a);
+        hipError_t e;
+        if (mode == kGatherFill)
+            e = launch(c, KVR_KERNEL_REFILL, gather_kernel<kGatherFill>, grid, dim3(NT), 0, s, a);
+        else if (mode == kGatherResident)
+            e = launch(c, KVR_KERNEL_GATHER, gather_kernel<kGatherResident>, grid, dim3(NT), 0, s, a);
+        else
+            e = launch(c, KVR_KERNEL_GATHER, gather_kernel<kGatherAll>, grid, dim3(NT), 0, s, a);
         if (e != hipSuccess)
             return e;
     }

@@ -348,9 +348,10 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
     return ok();
 }
 
-int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
-                    const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
-                    int32_t stride, void *const *out, int32_t *status, void *stream)
+static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
+                        int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                        const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                        void *stream)
 {
     if (int rc = check_ctx(ctx, false))
         return rc;
@@ -380,12 +381,39 @@ int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32
             targets[t].layer = layers[t0 + t];
             targets[t].out = static_cast<uint8_t *>(out[t0 + t]);
         }
-        hipError_t e = kvr::launch_gather(ctx, targets, nt, n, req_ids, loc, count, stride,
+        hipError_t e = kvr::launch_gather(ctx, mode, targets, nt, n, req_ids, loc, sel, count, stride,
                                           status, s);
         if (e != hipSuccess)
             rc = hip_fail(e, "gather launch");
     }
     return rc == KVR_OK ? ok() : rc;
+}
+
+int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                    const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
+                    int32_t stride, void *const *out, int32_t *status, void *stream)
+{
+    return gather_entry(ctx, kvr::kGatherAll, n_layers, layers, n, req_ids, loc, nullptr, count,
+                        stride, out, status, stream);
+}
+
+int kvr_gather_resident_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                             const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
+                             int32_t stride, void *const *out, int32_t *status, void *stream)
+{
+    return gather_entry(ctx, kvr::kGatherResident, n_layers, layers, n, req_ids, loc, nullptr,
+                        count, stride, out, status, stream);
+}
+
+int kvr_fill_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                         const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                         const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                         void *stream)
+{
+    if (n > 0 && stride > 0 && n_layers > 0 && !sel)
+        return fail(KVR_E_ARG, "sel is required");
+    return gather_entry(ctx, kvr::kGatherFill, n_layers, layers, n, req_ids, loc, sel, count,
+                        stride, out, status, stream);
 }
 
 int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,

@@ -16,9 +16,12 @@ constexpr int kMaxSelCap = 8192;
 constexpr int kMaxUnion = 8192;        // q * k of one verification block
 constexpr int kGatherLayersPerLaunch = 24;
 
-// Location word layout (bits 31..30 place, 29..0 index).
+// Location word layout (bits 31..30 place, 29..0 index; a hot-cache word
+// carries the fresh flag in bit 29 and the slot in bits 28..0).
 constexpr uint32_t kPlaceShift = 30;
 constexpr uint32_t kIndexMask = 0x3FFFFFFFu;
+constexpr uint32_t kFreshBit = KVR_LOC_FRESH;
+constexpr uint32_t kSlotMask = kFreshBit - 1;
 
 // Device-side pointers of one payload layer.
 struct LayerPtrs {
@@ -122,9 +125,13 @@ struct GatherTarget {
     int32_t layer;
     uint8_t *out;
 };
-hipError_t launch_gather(const kvr_ctx *c, const GatherTarget *targets, int32_t n_targets,
-                         int32_t n, const int32_t *req_ids, const uint32_t *loc,
-                         const int32_t *count, int32_t stride, int32_t *status, hipStream_t s);
+constexpr int32_t kGatherAll = 0;       // every valid word
+constexpr int32_t kGatherResident = 1;  // every valid word but fresh hot-cache rows
+constexpr int32_t kGatherFill = 2;      // fresh hot-cache rows, from host into slot and out
+hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *targets,
+                         int32_t n_targets, int32_t n, const int32_t *req_ids, const uint32_t *loc,
+                         const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,
+                         hipStream_t s);
 
 hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,
                          const uint8_t *new_rows, int32_t *status, hipStream_t s);

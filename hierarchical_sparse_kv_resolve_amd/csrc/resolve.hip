@@ -643,7 +643,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         uint32_t w = word[e];
         if (is_pending(w)) {
             const int32_t s = hv[e];
-            w = (2u << kPlaceShift) | (uint32_t)(s & kIndexMask);
+            w = (2u << kPlaceShift) | ((s & kFilledBit) ? kFreshBit : 0u) | (uint32_t)(s & kSlotMask);
             counts += (s & kFilledBit) ? (1ull << 48) : (1ull << 32);
         } else {
             counts += (w >> kPlaceShift) == 0 ? 1ull : (1ull << 16);

@@ -32,7 +32,8 @@ EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "
            "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_gather_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
            "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
-           "kvr_reclaim_pages", "kvr_restore_pages", "kvr_residency_create",
+           "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
+           "kvr_fill_gather_rows", "kvr_residency_create",
            "kvr_residency_destroy", "kvr_residency_admit", "kvr_residency_release",
            "kvr_residency_refill", "kvr_residency_counts")
 
@@ -78,6 +79,8 @@ def lib():
             "kvr_append_rows": [P, I, P, P, P, P],
             "kvr_resolve_rows": [P, I, P, P, P, I, P, P, P, I, P, P, P],
             "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
+            "kvr_gather_resident_rows": [P, I, P, I, P, P, P, I, P, P, P],
+            "kvr_fill_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
             "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
             "kvr_reuse_locations": [P, I, I, P, I, P, P, P, P, I, P, P, P, P],
             "kvr_status_summary": [P, I, P],
@@ -206,6 +209,24 @@ class Context:
         arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
         _check(lib().kvr_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
                                      _ptr(count), stride, arr_o, _ptr(status), _stream(stream)))
+
+    def gather_resident_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None,
+                             stream=None):
+        nl = len(layers)
+        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
+        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
+        _check(lib().kvr_gather_resident_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
+                                              _ptr(count), stride, arr_o, _ptr(status),
+                                              _stream(stream)))
+
+    def fill_gather_rows(self, layers, n, req_ids, loc, sel, count, stride, outs, status=None,
+                         stream=None):
+        nl = len(layers)
+        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
+        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
+        _check(lib().kvr_fill_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
+                                          _ptr(sel), _ptr(count), stride, arr_o, _ptr(status),
+                                          _stream(stream)))
 
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
         _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),

@@ -120,7 +120,7 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, prefetch_groups=0, serialize: bool = False):
+    def step(self, s: int, prefetch_groups=0, serialize: bool = False, fused: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
 
@@ -136,12 +136,22 @@ class GpuRun:
         and several resolving layers, each layer's fill and gather run on the
         side stream while the next layer resolves.
 
+        fused=True (prefetch_groups is then ignored): the host fill and the
+        gather of fresh rows are one pass (fill_gather_rows, side stream)
+        while every other row is gathered beside it (gather_resident_rows);
+        with one physical source and several resolving layers the resident
+        gathers run on a second side stream, each layer's fill waits for the
+        previous layer's resident gather (its victims may be slots that gather
+        reads) and each resident gather for the previous fill (its hits may be
+        slots that fill wrote).
+
         serialize=True issues the same launches but lets no two of them
         overlap, so launch timing (Context.timing_begin) sees each kernel
         running alone."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
         main = torch.cuda.current_stream()
+        last_filled = last_resident = None
         ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
         for g in range(cfg.groups):
             sel = self.sel_dev[s][g]
@@ -153,11 +163,41 @@ class GpuRun:
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            pipelined = bool(prefetch_groups)
+            pipelined = bool(prefetch_groups) or fused
             fill_layer = -1 if pipelined else 0
             ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
                              self.status[g], self.stats, stream=main)
-            if cfg.reuse != "distinct" and pipelined:
+            if fused:
+                resolved = torch.cuda.Event()
+                resolved.record(main)
+                side = self._side()
+                side.wait_event(resolved)
+                layers = list(range(self.nl)) if cfg.reuse == "distinct" else [0]
+                outs = self.outs[g] if cfg.reuse == "distinct" else self.outs[g][:1]
+                if cfg.reuse != "distinct" and last_resident is not None:
+                    side.wait_event(last_resident)
+                ctx.fill_gather_rows(layers, n, None, loc, src, count, stride, outs,
+                                     self.gather_status, stream=side)
+                filled = torch.cuda.Event()
+                filled.record(side)
+                res = main if cfg.reuse == "distinct" else self._side(2)
+                res.wait_event(resolved)
+                if serialize:
+                    res.wait_event(filled)
+                elif last_filled is not None:
+                    res.wait_event(last_filled)
+                ctx.gather_resident_rows(layers, n, None, loc, count, stride, outs,
+                                         self.gather_status, stream=res)
+                resident = torch.cuda.Event()
+                resident.record(res)
+                last_filled, last_resident = filled, resident
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=main)
+                if g == cfg.groups - 1 or serialize:
+                    main.wait_event(filled)
+                    main.wait_event(resident)
+            elif cfg.reuse != "distinct" and pipelined:
                 # One physical source: this layer's fill and gather run on the
                 # side stream while the main stream resolves the next layer
                 # (resolve touches metadata only).  The side stream keeps the
@@ -258,25 +298,33 @@ class GpuRun:
         for dst, src in zip(self.tail, snap["tail"]):
             dst.copy_(src)
 
-    def capture(self, steps, prefetch_groups=0):
+    def capture(self, steps, prefetch_groups=0, fused: bool = False):
         """Capture the launches of `steps` into one HIP graph (nothing runs
         until it is replayed).  Each replay runs those decode steps again from
         whatever state the buffers hold."""
         torch = self.torch
+        if fused and self.cfg.reuse != "distinct":
+            # Capturing this schedule (two side streams that wait on each
+            # other's events across resolving layers) ended in a host crash
+            # inside the graph runtime's capture end; until a cause is shown it
+            # is not captured.  The eager schedule is unaffected.
+            raise NotImplementedError("graph capture of the fused schedule for one physical "
+                                      "source with several resolving layers is disabled")
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()  # default priority
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
             with torch.cuda.graph(graph, stream=cap):
                 for s in steps:
-                    self.step(s, prefetch_groups=prefetch_groups)
+                    self.step(s, prefetch_groups=prefetch_groups, fused=fused)
         torch.cuda.current_stream().wait_stream(cap)
         return graph
 
-    def _side(self):
-        if getattr(self, "_side_stream", None) is None:
-            self._side_stream = self.torch.cuda.Stream()  # default priority
-        return self._side_stream
+    def _side(self, k: int = 1):
+        streams = self.__dict__.setdefault("_side_streams", {})
+        if k not in streams:
+            streams[k] = self.torch.cuda.Stream()  # default priority
+        return streams[k]
 
     # ------------------------------------------------------------------ read-back (syncs)
     def state(self) -> dict:

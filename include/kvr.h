@@ -41,7 +41,9 @@
  *
  * Location word (uint32): bits 31..30 give the place (kvr_place), bits 29..0
  * the index in it: the tail ring slot (pos mod T), the optional-pool row
- * (physical page * P + pos mod P) or the hot-cache slot.
+ * (physical page * P + pos mod P) or the hot-cache slot.  A hot-cache word
+ * carries KVR_LOC_FRESH (bit 29) when its row was copied from host memory by
+ * the call that wrote the word; its slot is then in bits 28..0.
  */
 #ifndef KVR_H
 #define KVR_H
@@ -71,6 +73,7 @@ typedef enum kvr_place {
 } kvr_place;
 
 #define KVR_LOC_INVALID 0xFFFFFFFFu
+#define KVR_LOC_FRESH (1u << 29)  /* hot-cache word: filled from host by this call */
 
 typedef enum kvr_reuse_mode {
     /* Reuse layers of one physical KV source: the location vector is inherited
@@ -189,8 +192,9 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
 /* Gather resolved rows into contiguous per-request buffers, for several
  * payload layers sharing one location vector:
  *   out[l] (device) [n][stride][R] for layers[l]; row j < cnt of request i is
- *   the R bytes at loc[i][j] in that layer.  Invalid locations leave the row
- *   untouched.
+ *   the R bytes at loc[i][j] in that layer (a fresh hot-cache row is read
+ *   from its slot, so its fill must have run).  Invalid locations leave the
+ *   row untouched.
  *   layers (host) int32 [n_layers]; out (host) array of n_layers device pointers
  *   loc (device) uint32 [n][stride]; count (device) int32 [n] or NULL (= stride)
  *   status (device) int32 [n] or NULL: set to KVR_E_RANGE for a request with a
@@ -198,6 +202,28 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
 int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
                     const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
                     int32_t stride, void *const *out, int32_t *status, void *stream);
+
+/* The same gather split in two so that host fills and HBM gathers overlap
+ * (same arguments as kvr_gather_rows; together the two write what
+ * kvr_gather_rows writes after the fills):
+ *   kvr_gather_resident_rows copies every row whose location is not a fresh
+ *     hot-cache word (tail, page, hot-cache hit).  It reads no slot a fill of
+ *     the same call writes, so it may run while those fills are in flight.
+ *   kvr_fill_gather_rows copies every fresh row once from the layer's pinned
+ *     host store into both the layer's hot-cache slot and the output: the
+ *     host fill of that layer and its gather in one pass over the host link.
+ *     sel (device) int32 [n][stride] is the selection the resolve call took
+ *     (entry j's row); it reads no tag, so a later resolve of the same
+ *     requests may run beside it.  Use it instead of fill_layer and
+ *     kvr_reuse_locations(KVR_REUSE_DISTINCT_PAYLOAD) for these layers;
+ *     repeated rows fetch their host copy once per repeat. */
+int kvr_gather_resident_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                             const int32_t *req_ids, const uint32_t *loc, const int32_t *count,
+                             int32_t stride, void *const *out, int32_t *status, void *stream);
+int kvr_fill_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                         const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                         const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                         void *stream);
 
 /* Verification block dedup ("Speculative state": queries share missing-row
  * retrieval).  Per request: union_rows[i][0..u) = the distinct rows of the q
