@@ -50,6 +50,11 @@ def parse():
     ap.add_argument("--prefetch-groups", default="2",
                     help="layer groups whose host fills overlap earlier gathers: a count "
                          "(equal groups, 0 = off) or comma-separated group sizes")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "prefetch", "fused"],
+                    help="fused: host fills and the gather of the rows they bring in as one "
+                         "pass beside the gather of all other rows; prefetch: fills in layer "
+                         "groups ahead of per-group gathers; auto: fused for several payload "
+                         "layers sharing the indices, else prefetch")
     ap.add_argument("--hot-slots", type=int, default=0,
                     help="hot-cache budget B per request (default: the workload's)")
     ap.add_argument("--scenario", default="", choices=["", "load_step"],
@@ -163,7 +168,7 @@ def gather_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(workload, prefetch_groups):
+def recorded_traffic(workload, schedule):
     """HBM bytes per gather launch measured by counters, or None."""
     try:
         with open(TRAFFIC_PROFILE) as f:
@@ -171,7 +176,7 @@ def recorded_traffic(workload, prefetch_groups):
     except OSError:
         return None
     fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
-    if (fields.get("workload") != workload or fields.get("prefetch_groups") != str(prefetch_groups)
+    if (fields.get("workload") != workload or fields.get("schedule") != schedule
             or fields.get("source_sha256") != gather_source_hash()):
         return None
     try:
@@ -376,8 +381,16 @@ def main():
     counts = rows_per_group(inputs, range(W, total))
     pg = args.prefetch_groups
     pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
+    # auto: fused where several payload layers share the indices (their
+    # resident gathers are big enough to hide under the fill pass); with one
+    # payload layer the refill in ascending row order reads the host faster
+    fused = args.schedule == "fused" or (args.schedule == "auto" and cfg.reuse == "distinct"
+                                         and cfg.payload_layers > 1)
+    if fused and cfg.reuse != "distinct" and not args.no_graph:
+        raise SystemExit("the fused schedule of one physical source is run eagerly only "
+                         "(--no-graph)")
     for s in range(W):
-        gpu.step(s, prefetch_groups=pg)
+        gpu.step(s, prefetch_groups=pg, fused=fused)
     torch.cuda.synchronize()
     snap = gpu.snapshot()
     stats_before = gpu.stats_dict()
@@ -388,12 +401,12 @@ def main():
     # so each recorded duration is one kernel running alone.
     gpu.ctx.timing_begin(64 * K + 64)
     for s in range(W, total):
-        gpu.step(s, prefetch_groups=pg, serialize=True)
+        gpu.step(s, prefetch_groups=pg, serialize=True, fused=fused)
     launches = launch_means_ms(gpu.ctx.timing_end())
     torch.cuda.synchronize()
     if not args.no_graph:
         gpu.restore(snap)
-        graph = gpu.capture(range(W, total), prefetch_groups=pg)
+        graph = gpu.capture(range(W, total), prefetch_groups=pg, fused=fused)
         torch.cuda.synchronize()
         log("captured the timed steps into one graph")
 
@@ -407,7 +420,7 @@ def main():
     start.record()
     if args.no_graph:
         for s in range(W, total):
-            gpu.step(s, prefetch_groups=pg)
+            gpu.step(s, prefetch_groups=pg, fused=fused)
     else:
         graph.replay()
     end.record()
@@ -443,24 +456,30 @@ def main():
     # block, whose rows are gathered once per union row
     sel_entries = K * cfg.groups * cfg.n_req * cfg.q * cfg.k * n_out
 
+    stats_all = gpu.stats_dict()
+    stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}
     # gather roofline: algorithmic bytes per launch = rows * (R read + R write) per
-    # payload layer + one 4-byte location word per row
+    # payload layer + one 4-byte location word per row.  In the fused schedule
+    # the gather kernel moves the resident rows (tail, page, hot hit) and reads
+    # every location word; the rows copied from host go through the fill pass.
     g_list = launches.get("gather", [])
     gather_calls = len(g_list)
-    bytes_gather = sum(v * (2 * cfg.R * n_out + 4) for v in counts.values()) / max(1, gather_calls)
+    entries = sum(counts.values())
+    moved = entries - stats["miss"] if fused else entries
+    bytes_gather = (moved * 2 * cfg.R * n_out + entries * 4) / max(1, gather_calls)
     g_ms = sum(g_list) / max(1, gather_calls)
     achieved = bytes_gather / (g_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(cfg.name, args.prefetch_groups),
-                "kernel": "gather_kernel", "bytes_per_launch": int(bytes_gather),
+                "traffic": recorded_traffic(cfg.name, "fused" if fused
+                                            else f"prefetch:{args.prefetch_groups}"),
+                "kernel": "gather_kernel<resident>" if fused else "gather_kernel<all>",
+                "bytes_per_launch": int(bytes_gather),
                 "launch_us": round(g_ms * 1e3, 2),
                 "timing": "start/end events of each gather dispatch (hipExtLaunchKernel) in an "
                           "eager pass over the same timed steps and launches from the same "
                           "starting state, no two kernels overlapping"}
 
-    stats_all = gpu.stats_dict()
-    stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}
     found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
     split = {"step1_tail_or_page": round((stats["tail"] + stats["page"]) / found, 4),
              "step2_hot_hit": round(stats["hit"] / found, 4),
@@ -487,7 +506,8 @@ def main():
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(wall_s * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-        "config": {"workload": cfg.name, "prefetch_groups": args.prefetch_groups,
+        "config": {"workload": cfg.name, "schedule": "fused" if fused else "prefetch",
+                   "prefetch_groups": None if fused else args.prefetch_groups,
                    "launch": "eager" if args.no_graph else "hip_graph", "n_req": cfg.n_req, "history_rows": cfg.H,
                    "row_bytes": cfg.R, "page_rows": cfg.P, "tail_rows": cfg.T,
                    "ready_frac": cfg.ready_frac, "hot_slots": cfg.B, "top_k": cfg.k,

@@ -10,10 +10,10 @@
 //   all       every valid word (fresh hot-cache rows read from their slots);
 //   resident  every valid word except fresh hot-cache rows; it reads no slot
 //             a fill of the same call writes, so it runs beside the fills;
-//   fill      only fresh hot-cache rows: each is read once from the layer's
-//             pinned host store (its row is the selection entry's) and
-//             written both to the slot (the host fill of step 3 of
-//             "Resolution") and to the output, one pass over the host link
+//   fill      (fill_kernel) only fresh hot-cache rows: each is read once from
+//             the layer's pinned host store (its row is the selection
+//             entry's) and written both to the slot (the host fill of step 3
+//             of "Resolution") and to the output, one pass over the host link
 //             for both.  It reads the selection, not the tags, so a later
 //             resolve of the same requests may already be rewriting tags.
 #include "kvr_internal.h"
@@ -23,6 +23,10 @@ namespace kvr {
 namespace {
 
 constexpr int NT = kRowThreads;
+// Fill workers per launch, over all its layers (at most one per job): enough
+// jobs in flight to keep the host link busy, few enough that the resident
+// gather running beside them keeps its compute units.
+constexpr int kFillWorkers = 512;
 
 struct GatherArgs {
     Shape sh;
@@ -64,9 +68,6 @@ template <int MODE>
 __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 {
     __shared__ const uint8_t *sSrc[kMaxTileRows];
-    __shared__ uint8_t *sOut[kMaxTileRows];  // fill mode
-    __shared__ uint8_t *sHot[kMaxTileRows];  // fill mode
-    __shared__ int sRows;
     const int i = blockIdx.y;
     const int t = blockIdx.z;
     const int r = a.req_ids ? a.req_ids[i] : i;
@@ -79,45 +80,16 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
     const LayerPtrs lp = a.layers[a.layer[t]];
     const int R = a.sh.R;
     uint8_t *dst = a.out[t] + ((int64_t)i * a.stride + j0) * R;
-    int rows = nrows;
-    if (MODE == kGatherFill) {
-        // compact this tile's fresh rows (their order does not matter: each
-        // has its own destinations)
-        if (threadIdx.x == 0)
-            sRows = 0;
-        __syncthreads();
-        if ((int)threadIdx.x < nrows) {
-            const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
-            const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
-            if (w != KVR_LOC_INVALID && place == KVR_PLACE_HOT && (idx & kFreshBit)) {
-                const uint32_t slot = idx & kSlotMask;
-                const int32_t row = a.sel[(int64_t)i * a.stride + j0 + threadIdx.x];
-                if (slot < (uint32_t)a.sh.B && row >= 0 && (int64_t)row < a.sh.host_rows) {
-                    const int k = atomicAdd(&sRows, 1);
-                    sSrc[k] = lp.host + ((int64_t)r * a.sh.host_rows + row) * R;
-                    sHot[k] = lp.hot + ((int64_t)r * a.sh.B + slot) * R;
-                    sOut[k] = dst + (int64_t)threadIdx.x * R;
-                } else if (a.status) {
-                    a.status[i] = KVR_E_RANGE;
-                }
-            }
-        }
-        __syncthreads();
-        rows = sRows;
-        if (rows == 0)
-            return;
-    } else {
-        if ((int)threadIdx.x < nrows) {
-            const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
-            bool bad;
-            sSrc[threadIdx.x] = resident_src(a, lp, r, w, MODE == kGatherResident, bad);
-            if (bad && a.status)
-                a.status[i] = KVR_E_RANGE;
-        }
-        __syncthreads();
+    if ((int)threadIdx.x < nrows) {
+        const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
+        bool bad;
+        sSrc[threadIdx.x] = resident_src(a, lp, r, w, MODE == kGatherResident, bad);
+        if (bad && a.status)
+            a.status[i] = KVR_E_RANGE;
     }
+    __syncthreads();
     const int C = a.ts.chunks;
-    const int total = rows * C;
+    const int total = nrows * C;
     for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
         u32x4 v[kUnroll];
         int rr[kUnroll];
@@ -139,12 +111,77 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
             if (rr[u] < 0)
                 continue;
             const int c = c0 + u * NT + threadIdx.x;
-            if (MODE == kGatherFill) {
-                const int off = (c - rr[u] * C) * 16;
+            store_chunk_nt(dst + (int64_t)c * 16, v[u]);
+        }
+    }
+}
+
+// Fill pass: a bounded grid (workers x layers) strides over (request, tile of
+// kFillTile entries) jobs, so the host link is kept busy by a few workers
+// with many loads in flight while the other compute units gather resident
+// rows.  Each job compacts its fresh rows in LDS (their order does not matter:
+// each row has its own two destinations), then streams them.
+constexpr int kFillTile = 1024;
+
+__global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32_t tiles_per_req)
+{
+    __shared__ const uint8_t *sSrc[kFillTile];
+    __shared__ uint8_t *sHot[kFillTile];
+    __shared__ uint8_t *sOut[kFillTile];
+    __shared__ int sRows;
+    const int t = blockIdx.y;
+    const LayerPtrs lp = a.layers[a.layer[t]];
+    const int R = a.sh.R;
+    const int C = a.ts.chunks;
+    for (int64_t job = blockIdx.x; job < (int64_t)n * tiles_per_req; job += gridDim.x) {
+        const int i = (int)(job / tiles_per_req);
+        const int j0 = (int)(job - (int64_t)i * tiles_per_req) * kFillTile;
+        const int r = a.req_ids ? a.req_ids[i] : i;
+        int cnt = a.count ? a.count[i] : a.stride;
+        cnt = cnt < 0 ? 0 : (cnt > a.stride ? a.stride : cnt);
+        if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
+            continue;  // uniform across the workgroup
+        const int j1 = min(j0 + kFillTile, cnt);
+        __syncthreads();  // the previous job is done with the lists
+        if (threadIdx.x == 0)
+            sRows = 0;
+        __syncthreads();
+        uint8_t *dst = a.out[t] + (int64_t)i * a.stride * R;
+        for (int j = j0 + threadIdx.x; j < j1; j += NT) {
+            const uint32_t w = a.loc[(int64_t)i * a.stride + j];
+            const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
+            if (w == KVR_LOC_INVALID || place != KVR_PLACE_HOT || !(idx & kFreshBit))
+                continue;
+            const uint32_t slot = idx & kSlotMask;
+            const int32_t row = a.sel[(int64_t)i * a.stride + j];
+            if (slot < (uint32_t)a.sh.B && row >= 0 && (int64_t)row < a.sh.host_rows) {
+                const int k = atomicAdd(&sRows, 1);
+                sSrc[k] = lp.host + ((int64_t)r * a.sh.host_rows + row) * R;
+                sHot[k] = lp.hot + ((int64_t)r * a.sh.B + slot) * R;
+                sOut[k] = dst + (int64_t)j * R;
+            } else if (a.status) {
+                a.status[i] = KVR_E_RANGE;
+            }
+        }
+        __syncthreads();
+        const int total = sRows * C;
+        for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
+            u32x4 v[kUnroll];
+            int rr[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int c = c0 + u * NT + threadIdx.x;
+                rr[u] = c < total ? c / C : -1;
+                if (rr[u] >= 0)
+                    load_chunk(v[u], sSrc[rr[u]] + (c - rr[u] * C) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (rr[u] < 0)
+                    continue;
+                const int off = (c0 + u * NT + (int)threadIdx.x - rr[u] * C) * 16;
                 store_chunk(sHot[rr[u]] + off, v[u]);
                 store_chunk_nt(sOut[rr[u]] + off, v[u]);
-            } else {
-                store_chunk_nt(dst + (int64_t)c * 16, v[u]);
             }
         }
     }
@@ -175,9 +212,14 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
         }
         dim3 grid((stride + a.ts.rows - 1) / a.ts.rows, n, nt);
         hipError_t e;
-        if (mode == kGatherFill)
-            e = launch(c, KVR_KERNEL_REFILL, gather_kernel<kGatherFill>, grid, dim3(NT), 0, s, a);
-        else if (mode == kGatherResident)
+        if (mode == kGatherFill) {
+            const int tiles_per_req = (stride + kFillTile - 1) / kFillTile;
+            const int64_t jobs = (int64_t)n * tiles_per_req;
+            int64_t workers = (kFillWorkers + nt - 1) / nt;
+            workers = workers < jobs ? workers : jobs;
+            dim3 fgrid((unsigned)(workers > 0 ? workers : 1), nt);
+            e = launch(c, KVR_KERNEL_REFILL, fill_kernel, fgrid, dim3(NT), 0, s, a, n, tiles_per_req);
+        } else if (mode == kGatherResident)
             e = launch(c, KVR_KERNEL_GATHER, gather_kernel<kGatherResident>, grid, dim3(NT), 0, s, a);
         else
             e = launch(c, KVR_KERNEL_GATHER, gather_kernel<kGatherAll>, grid, dim3(NT), 0, s, a);
