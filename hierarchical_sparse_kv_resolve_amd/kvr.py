@@ -35,7 +35,10 @@ EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "
            "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
            "kvr_fill_gather_rows", "kvr_residency_create",
            "kvr_residency_destroy", "kvr_residency_admit", "kvr_residency_release",
-           "kvr_residency_refill", "kvr_residency_counts")
+           "kvr_residency_refill", "kvr_residency_counts", "kvr_draft_create",
+           "kvr_draft_destroy", "kvr_draft_reset", "kvr_draft_append", "kvr_draft_rollback",
+           "kvr_draft_window", "kvr_staging_create", "kvr_staging_destroy",
+           "kvr_staging_acquire", "kvr_staging_release")
 
 # kvr_kernel: kinds of the library's kernel launches (launch timing).
 KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state")
@@ -96,6 +99,16 @@ def lib():
             "kvr_residency_release": [P, I],
             "kvr_residency_refill": [P, I, I, P, P, P, P],
             "kvr_residency_counts": [P, P, P, P],
+            "kvr_draft_create": [I, I, I, I, P, P, P, P],
+            "kvr_draft_destroy": [P],
+            "kvr_draft_reset": [P, P],
+            "kvr_draft_append": [P, I, P, I, P, P, P],
+            "kvr_draft_rollback": [P, I, P, P, P, P],
+            "kvr_draft_window": [P, I, P, P, P, P, P],
+            "kvr_staging_create": [I, P],
+            "kvr_staging_destroy": [P],
+            "kvr_staging_acquire": [P, P, P],
+            "kvr_staging_release": [P, I, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -335,3 +348,69 @@ class Residency:
         _check(lib().kvr_residency_counts(self.handle, ctypes.byref(f), ctypes.byref(r),
                                           ctypes.byref(s)))
         return f.value, r.value, s.value
+
+
+class DraftRing:
+    """Drafter visible-window ring (kvr_draft_*) over caller-owned device
+    buffers: ring [n_req][capacity][row_bytes], length and high int32 [n_req]."""
+
+    def __init__(self, n_req, window, capacity, row_bytes, ring, length, high):
+        h = ctypes.c_void_p()
+        _check(lib().kvr_draft_create(n_req, window, capacity, row_bytes, _ptr(ring), _ptr(length),
+                                      _ptr(high), ctypes.byref(h)))
+        self.handle = h.value
+
+    def close(self):
+        if self.handle:
+            lib().kvr_draft_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self, stream=None):
+        _check(lib().kvr_draft_reset(self.handle, _stream(stream)))
+
+    def append(self, n, req_ids, rows_each, rows, status=None, stream=None):
+        _check(lib().kvr_draft_append(self.handle, n, _ptr(req_ids), rows_each, _ptr(rows),
+                                      _ptr(status), _stream(stream)))
+
+    def rollback(self, n, req_ids, keep, status=None, stream=None):
+        _check(lib().kvr_draft_rollback(self.handle, n, _ptr(req_ids), _ptr(keep), _ptr(status),
+                                        _stream(stream)))
+
+    def window(self, n, req_ids, out, visible=None, status=None, stream=None):
+        _check(lib().kvr_draft_window(self.handle, n, _ptr(req_ids), _ptr(out), _ptr(visible),
+                                      _ptr(status), _stream(stream)))
+
+
+class StagingPool:
+    """Verification staging reuse (kvr_staging_*): buffer indices handed out
+    round-robin; acquire waits for the buffer's last release."""
+
+    def __init__(self, n_buffers: int):
+        h = ctypes.c_void_p()
+        _check(lib().kvr_staging_create(n_buffers, ctypes.byref(h)))
+        self.handle = h.value
+
+    def close(self):
+        if self.handle:
+            lib().kvr_staging_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def acquire(self, stream=None) -> int:
+        idx = ctypes.c_int32()
+        _check(lib().kvr_staging_acquire(self.handle, _stream(stream), ctypes.byref(idx)))
+        return idx.value
+
+    def release(self, index: int, stream=None):
+        _check(lib().kvr_staging_release(self.handle, index, _stream(stream)))

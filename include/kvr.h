@@ -327,6 +327,59 @@ int kvr_residency_refill(kvr_residency *res, int32_t bound, int32_t cap, int32_t
 int kvr_residency_counts(const kvr_residency *res, int64_t *free_pages, int64_t *ready_pages,
                          int64_t *reserved_pages);
 
+/* Speculative state ("Adaptive DHiSparse", section "How it works",
+ * paragraph "Speculative state").
+ *
+ * Drafter visible-window ring: the drafter keeps only its visible window.  Per
+ * request, drafter rows are numbered by position; row p lives in slot p mod C
+ * of a ring of C >= W slots; the visible window is the last min(W, length)
+ * positions.  The C - W extra slots let rows that verification rejects be
+ * dropped: a rollback to a shorter length is allowed while no position
+ * written since (kept or dropped) has overwritten the window it leaves
+ * visible, i.e. for keep >= (highest position ever written + 1) - (C - W).
+ *   kvr_draft_create: ring (device) [n_req][C][row_bytes] (row_bytes a
+ *     multiple of 16), length and high (device) int32 [n_req] (rows kept, and
+ *     highest position ever written + 1); all caller-owned; the current device
+ *     is the ring's.  kvr_draft_reset zeroes length and high (stream-ordered).
+ *   kvr_draft_append: rows (device) [n][rows_each][row_bytes], rows_each <= C,
+ *     appended at positions length .. length + rows_each - 1.
+ *   kvr_draft_rollback: keep (device) int32 [n]; status KVR_E_RANGE (nothing
+ *     changes) when keep is above the length or below the rollback limit.
+ *   kvr_draft_window: out (device) [n][W][row_bytes] receives the visible rows
+ *     oldest first (rows past the window are untouched); visible (device)
+ *     int32 [n] or NULL receives their number.
+ *   status (device) int32 [n] or NULL: KVR_E_ARG for a request out of range.
+ * req_ids (device) int32 [n] or NULL (= 0 .. n-1) name each request at most
+ * once per call.  All calls enqueue one kernel on `stream` and never
+ * synchronise the host. */
+typedef struct kvr_draft kvr_draft;
+
+int kvr_draft_create(int32_t n_req, int32_t window, int32_t capacity, int32_t row_bytes,
+                     void *ring, int32_t *length, int32_t *high, kvr_draft **out);
+int kvr_draft_destroy(kvr_draft *d);
+int kvr_draft_reset(kvr_draft *d, void *stream);
+int kvr_draft_append(kvr_draft *d, int32_t n, const int32_t *req_ids, int32_t rows_each,
+                     const void *rows, int32_t *status, void *stream);
+int kvr_draft_rollback(kvr_draft *d, int32_t n, const int32_t *req_ids, const int32_t *keep,
+                       int32_t *status, void *stream);
+int kvr_draft_window(kvr_draft *d, int32_t n, const int32_t *req_ids, void *out,
+                     int32_t *visible, int32_t *status, void *stream);
+
+/* Verification staging reuse: target layers reuse staging buffers once their
+ * consumers complete.  A pool of n_buffers caller-owned buffers, named by
+ * index and handed out round-robin.  kvr_staging_acquire makes `stream` wait
+ * until the buffer's previous consumer has released it; kvr_staging_release
+ * records that release on the consumer's stream after its last read of the
+ * buffer.  Host object, not thread-safe; acquire and release enqueue only an
+ * event wait or record.  Not meant for graph capture (a release recorded
+ * before the capture is not visible to it). */
+typedef struct kvr_staging kvr_staging;
+
+int kvr_staging_create(int32_t n_buffers, kvr_staging **out);
+int kvr_staging_destroy(kvr_staging *p);
+int kvr_staging_acquire(kvr_staging *p, void *stream, int32_t *index);
+int kvr_staging_release(kvr_staging *p, int32_t index, void *stream);
+
 /* Host helper, after the caller has synchronised and copied status to host:
  * number of failed requests; *first_bad = index of the first (or -1). */
 int kvr_status_summary(const int32_t *status, int32_t n, int32_t *first_bad);

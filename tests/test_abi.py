@@ -68,3 +68,15 @@ def test_timing_calls_reject_a_null_context():
     lib = kvr.lib()
     assert lib.kvr_timing_begin(None, 8) == kvr.E_ARG
     assert lib.kvr_timing_end(None, 0, None, None, None) == kvr.E_ARG
+
+
+def test_speculative_state_rejects_bad_shapes():
+    lib = kvr.lib()
+    out = ctypes.c_void_p()
+    # window 0; capacity below the window; rows not a multiple of 16
+    for args in ((2, 0, 4, 64), (2, 5, 4, 64), (2, 4, 8, 24)):
+        assert lib.kvr_draft_create(*args, 1, 1, 1, ctypes.byref(out)) == kvr.E_ARG
+    assert lib.kvr_draft_append(None, 0, None, 0, None, None, None) == kvr.E_ARG
+    assert lib.kvr_staging_create(0, ctypes.byref(out)) == kvr.E_ARG
+    assert lib.kvr_staging_acquire(None, None, None) == kvr.E_ARG
+    assert lib.kvr_staging_release(None, 0, None) == kvr.E_ARG
