@@ -201,6 +201,27 @@ def copy_calibration(torch, nbytes=1 << 30, reps=3):
                       "kernels": ["copy_", "bitwise_not"]}), flush=True)
 
 
+def device_copy_gbs(torch, nbytes=4 << 30, reps=3):
+    """Best rate (read + write bytes) of a plain device-to-device copy of
+    nbytes through torch (the runtime's copy kernel), far larger than the
+    last-level cache: what a streaming copy reaches on this HBM."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
 def zero_copy_read_gbs(torch, gpu, reps=3):
     """Sequential zero-copy read rate of the pinned host stores by the refill
     kernel itself: every request's first B host rows, in order, into its B hot
@@ -491,6 +512,8 @@ def main():
     host_bytes = stats["fill"] * cfg.R * fill_layers
     fill_calls = launches.get("refill", [])
     fill_s = sum(fill_calls) * 1e-3
+    roofline["device_copy_gbs"] = round(device_copy_gbs(torch), 1)
+    roofline["frac_of_device_copy"] = round(achieved / roofline["device_copy_gbs"], 4)
     copy_gbs = host_link_gbs(torch)
     seq_gbs = zero_copy_read_gbs(torch, gpu)
     link = max(copy_gbs, seq_gbs)
