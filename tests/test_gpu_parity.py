@@ -515,3 +515,62 @@ def test_launch_timing_records_each_kernel():
         compare(run.step(4))
     finally:
         gpu.close()
+
+
+@pytest.mark.parametrize("c,kw", [(2, dict()), (4, dict(fused=True)), (5, dict(prefetch_groups=2))])
+def test_snapshot_resume_equals_continuous_run(c, kw):
+    """Copy the state after step s, scramble it, restore it and run steps
+    s..S-1: every output and the final state equal those of the continuous
+    run (and the oracle's)."""
+    import torch
+    cfg = tiny(c).with_(steps=6)
+    s_cut = 3
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    a = _gpu_run(inputs)
+    b = _gpu_run(inputs)
+    try:
+        a.stage(range(cfg.steps))
+        b.stage(range(cfg.steps))
+        for s in range(s_cut):
+            b.step(s, **kw)
+        torch.cuda.synchronize()
+        snap = b.snapshot()
+        b.tag.fill_(-1)
+        b.stamp.fill_(0)
+        b.clock.fill_(123)
+        for h in b.hot:
+            h.fill_(0x5A)
+        for t in b.tail:
+            t.fill_(0x5A)
+        b.L.fill_(0)
+        b.restore(snap)
+        for s in range(cfg.steps):
+            o = run.step(s)
+            a.step(s, **kw)
+            if s >= s_cut:
+                b.step(s, **kw)
+                for g in range(cfg.groups):
+                    ga, gb = a.group(g), b.group(g)
+                    for key in ("fill_count", "status"):
+                        assert np.array_equal(ga[key], gb[key]), (s, g, key)
+                    # only what the calls wrote: entries up to each request's
+                    # count, fills up to its fill count
+                    cnt = ga["union_count"] if cfg.q > 1 else [ga["loc"].shape[1]] * cfg.n_req
+                    for r in reqs:
+                        n, f = cnt[r], ga["fill_count"][r]
+                        assert np.array_equal(ga["loc"][r, :n], gb["loc"][r, :n]), (s, g, r)
+                        assert np.array_equal(ga["fills"][r, :f], gb["fills"][r, :f]), (s, g, r)
+                        for oa, ob in zip(ga["out"], gb["out"]):
+                            assert np.array_equal(oa[r, :n], ob[r, :n]), (s, g, r)
+                    _compare_group(cfg, gb, o["groups"][g], reqs)
+        sa, sb = a.state(), b.state()
+        for key in sa:
+            assert np.array_equal(sa[key], sb[key]), key
+        _compare_state(b, run, reqs)
+        for ha, hb in zip(a.hot, b.hot):
+            assert torch.equal(ha, hb)
+    finally:
+        a.close()
+        b.close()

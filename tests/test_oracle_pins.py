@@ -17,6 +17,8 @@ from collections import OrderedDict
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 from oracle import oracle as orc
 from oracle.runner import OracleRun
@@ -180,6 +182,41 @@ def test_oracle_equals_brute_force(chunk):
                                                          16, seed).reshape(k, 16))
         assert src.check()[0] & ~1 == 0
     assert counts.get(0, 0) > 500 and counts.get(orc.E_CAPACITY, 0) > 10
+
+
+@settings(max_examples=400, deadline=None, derandomize=True, database=None)
+@given(B=st.integers(1, 4), T=st.integers(0, 2), P=st.sampled_from([1, 2, 4]),
+       H=st.integers(1, 64), data=st.data())
+def test_oracle_equals_brute_force_hypothesis(B, T, P, H, data):
+    """The same comparison with shapes and calls drawn by hypothesis (shrinks a
+    failing case to a minimal one): B in 1..4, T in 0..2, P in {1, 2, 4},
+    H <= 64, up to 20 calls of k <= 8 rows."""
+    n_pages, full = -(-H // P), H // P
+    ready = data.draw(st.lists(st.booleans(), min_size=full, max_size=full))
+    page_map = np.full(n_pages, -1, dtype=np.int32)
+    ids = iter(range(full))
+    for p, rd in enumerate(ready):
+        if rd:
+            page_map[p] = next(ids)
+    host_valid = np.where(page_map >= 0, 0, 1).astype(np.uint8)
+    src = one_request_source(H, P, T, B, page_map, host_valid, R=16, n_layers=1, max_new=20,
+                             seed=5)
+    bf = BruteSource(H, P, T, B, page_map, host_valid, n_layers=1)
+    for _ in range(data.draw(st.integers(1, 20))):
+        if data.draw(st.booleans()) and src.L[0] < H + 20:
+            assert src.append(new_row(src, int(src.L[0]), seed=5))[0] == orc.OK
+            bf.append()
+        L = int(src.L[0])
+        sel = data.draw(st.lists(st.integers(0, L - 1), max_size=8))
+        loc, fills, fc, st_ = src.resolve(np.array([sel], dtype=np.int32).reshape(1, len(sel)))
+        bst, bloc, bfills = bf.resolve(sel)
+        assert st_[0] == bst
+        assert src.tag[0].tolist() == bf.tags() and src.stamp[0].tolist() == bf.stamps()
+        assert int(src.clock[0]) == bf.clock
+        assert fills[0, :fc[0]].tolist() == [list(f) for f in bfills]
+        if bst == orc.OK:
+            assert loc[0].tolist() == [word(p, i) for p, i in bloc]
+        assert src.check()[0] == 0
 
 
 # ----------------------------------------------------------------- textbook LRU
