@@ -55,6 +55,8 @@ def parse():
                          "pass beside the gather of all other rows; prefetch: fills in layer "
                          "groups ahead of per-group gathers; auto: fused for several payload "
                          "layers sharing the indices, else prefetch")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of the K steps from the same state (median reported)")
     ap.add_argument("--hot-slots", type=int, default=0,
                     help="hot-cache budget B per request (default: the workload's)")
     ap.add_argument("--scenario", default="", choices=["", "load_step"],
@@ -90,14 +92,26 @@ def rows_per_group(inputs, steps):
     return out
 
 
-def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0):
-    """The oracle as it stands, on this host's cores, over the same decode
-    steps from a fresh state; the pass is repeated (state restored) until at
-    least `min_s` seconds of work, and stops early at `budget_s`."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None):
+    """The oracle as it stands, on this host's cores (or `threads` of them),
+    over the same decode steps from a fresh state; the pass is repeated (state
+    restored) until at least `min_s` seconds of work, and stops early at
+    `budget_s`."""
     from oracle.runner import OracleRun
     from synth import Inputs
     inputs = Inputs(cfg, max_new=total_steps)
-    run = OracleRun(inputs)
+    run = OracleRun(inputs, threads=threads)
     src = run.src
     snap = src.snapshot()
     sels = {s: [inputs.selections(s, g) for g in range(cfg.groups)] for s in range(total_steps)}
@@ -431,44 +445,53 @@ def main():
         torch.cuda.synchronize()
         log("captured the timed steps into one graph")
 
-    # Pass 2 (timed): the K decode steps from the same starting state.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
-        gpu.restore(snap)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    if args.no_graph:
-        for s in range(W, total):
-            gpu.step(s, prefetch_groups=pg, fused=fused)
-    else:
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_s = t1 - t0
-    log(f"timed {K} steps in {wall_s * 1e3:.3f} ms")
-    gpu_ms = start.elapsed_time(end)
-
-    # every request of every timed call must have resolved
-    for g in range(cfg.groups):
-        st = gpu.status[g].cpu().numpy()
-        if (st != 0).any():
-            raise SystemExit(f"resolve failed: status {st.tolist()}")
-    if (gpu.gather_status.cpu().numpy() != 0).any() or (gpu.append_status.cpu().numpy() != 0).any():
-        raise SystemExit("gather or append reported an error")
-    # spot check of the last step against the payload closed form
+    # Pass 2 (timed): the K decode steps from the same starting state, run
+    # `repeats` times (state restored before each); every run is checked and
+    # the median is reported.
     from synth import payload_np
-    last = total - 1
-    rec = gpu.group(cfg.groups - 1)
-    sel = inputs.selections(last, cfg.groups - 1)
-    rows_src = rec["union"] if cfg.q > 1 else sel[:, 0, :]
-    for r in range(0, cfg.n_req, max(1, cfg.n_req // 4)):
-        j = np.arange(0, 64)
-        for l, out in enumerate(rec["out"]):
-            if not np.array_equal(out[r, j], payload_np(l, r, rows_src[r, j], cfg.R, cfg.seed)):
-                raise SystemExit("gathered bytes differ from the payload closed form")
+
+    def check_run():
+        # every request of every timed call must have resolved
+        for g in range(cfg.groups):
+            st = gpu.status[g].cpu().numpy()
+            if (st != 0).any():
+                raise SystemExit(f"resolve failed: status {st.tolist()}")
+        if ((gpu.gather_status.cpu().numpy() != 0).any()
+                or (gpu.append_status.cpu().numpy() != 0).any()):
+            raise SystemExit("gather or append reported an error")
+        # spot check of the last step against the payload closed form
+        last = total - 1
+        rec = gpu.group(cfg.groups - 1)
+        sel = inputs.selections(last, cfg.groups - 1)
+        rows_src = rec["union"] if cfg.q > 1 else sel[:, 0, :]
+        for r in range(0, cfg.n_req, max(1, cfg.n_req // 4)):
+            j = np.arange(0, 64)
+            for l, out in enumerate(rec["out"]):
+                if not np.array_equal(out[r, j], payload_np(l, r, rows_src[r, j], cfg.R, cfg.seed)):
+                    raise SystemExit("gathered bytes differ from the payload closed form")
+
+    walls, gpu_mss = [], []
+    for rep in range(max(1, args.repeats)):
+        if rep > 0 or args.no_graph:
+            gpu.restore(snap)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        if args.no_graph:
+            for s in range(W, total):
+                gpu.step(s, prefetch_groups=pg, fused=fused)
+        else:
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        gpu_mss.append(start.elapsed_time(end))
+        log(f"run {rep}: timed {K} steps in {walls[-1] * 1e3:.3f} ms")
+        check_run()
+    wall_s = float(np.median(walls))
+    gpu_ms = float(np.median(gpu_mss))
 
     n_out = cfg.payload_layers if cfg.reuse == "distinct" else 1
     rows_total = sum(counts.values()) * n_out
@@ -528,6 +551,7 @@ def main():
         "metric": "selected rows resolved+gathered/sec and achieved HBM GB/s (% of peak), 1 GPU",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(wall_s * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
+        "repeats": len(walls), "ms_per_step_runs": [round(w * 1e3 / K, 4) for w in walls],
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": cfg.name, "schedule": "fused" if fused else "prefetch",
                    "prefetch_groups": None if fused else args.prefetch_groups,
@@ -548,6 +572,10 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline(cfg, total, args.cpu_budget_s)
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
+        one = cpu_baseline(cfg, total, args.cpu_budget_s / 2, min_s=4.0, threads=1)
+        line["cpu_baseline"]["single_core"] = {"value": one["value"], "unit": one["unit"],
+                                               "sample": one["sample"]}
     print(json.dumps(line), flush=True)
 
 
