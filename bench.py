@@ -138,7 +138,9 @@ def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None):
                 break
         spent += time.perf_counter() - t0
         passes += 1
-    return {"value": round(rows / spent, 1), "unit": "rows/s", "cores": int(src.threads),
+    # the oracle runs one thread per request shard: at most n_req of them
+    return {"value": round(rows / spent, 1), "unit": "rows/s",
+            "cores": int(min(src.threads, cfg.n_req)),
             "kind": "oracle",
             "sample": f"{cfg.name}: {passes} pass(es) over decode steps 0..{total_steps - 1} of all "
                       f"{cfg.n_req} requests from a fresh state, {steps_done} steps, "
