@@ -199,6 +199,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     __shared__ int sMiss;
     __shared__ int sRangeErr;
     __shared__ int sHostErr;
+    __shared__ unsigned long long sStat;
 
     const Shape &sh = a.sh;
     const int i = blockIdx.x;
@@ -250,6 +251,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         sMiss = 0;
         sRangeErr = 0;
         sHostErr = 0;
+        sStat = 0;
     }
     __syncthreads();
 
@@ -651,15 +653,22 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         loc[j] = w;
     }
     if (a.stats) {
+        // The counters are summed in LDS first and one thread per workgroup
+        // adds them: device-scope atomics on one address from every wave of
+        // every workgroup are serialized in the memory system and kept the
+        // kernel from completing long after its last wave.  A workgroup's
+        // fields stay below 2^16 (at most 8 * 1024 entries).
         const unsigned long long wsum = wave_sum((unsigned long long)counts);
         unsigned long long *stp = reinterpret_cast<unsigned long long *>(a.stats);
-        if (lane_id() == 0 && wsum) {
-            atomicAdd(&stp[1], wsum & 0xFFFF);
-            atomicAdd(&stp[2], (wsum >> 16) & 0xFFFF);
-            atomicAdd(&stp[3], (wsum >> 32) & 0xFFFF);
-            atomicAdd(&stp[4], (wsum >> 48) & 0xFFFF);
-        }
+        if (lane_id() == 0 && wsum)
+            atomicAdd(&sStat, wsum);
+        __syncthreads();
         if (tid == 0) {
+            const unsigned long long tot = sStat;
+            atomicAdd(&stp[1], tot & 0xFFFF);
+            atomicAdd(&stp[2], (tot >> 16) & 0xFFFF);
+            atomicAdd(&stp[3], (tot >> 32) & 0xFFFF);
+            atomicAdd(&stp[4], (tot >> 48) & 0xFFFF);
             atomicAdd(&stp[0], 1ull);
             atomicAdd(&stp[5], (unsigned long long)m_total);
             if (a.count_host_bytes)
