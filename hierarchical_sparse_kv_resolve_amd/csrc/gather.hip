@@ -16,6 +16,10 @@
 //             of "Resolution") and to the output, one pass over the host link
 //             for both.  It reads the selection, not the tags, so a later
 //             resolve of the same requests may already be rewriting tags.
+//   fused     (fused_gather_kernel) fill and resident in one launch: the
+//             first workgroups of the grid are fill workers, the rest gather
+//             resident tiles, so the two share the chip without the
+//             cross-queue waits that two concurrent launches need.
 #include "kvr_internal.h"
 #include "rows.h"
 
@@ -64,18 +68,17 @@ __device__ __forceinline__ const uint8_t *resident_src(const GatherArgs &a, cons
     return nullptr;
 }
 
+// Tile x (kMaxTileRows or fewer whole rows) of request entry i into target t.
 template <int MODE>
-__global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
+__device__ __forceinline__ void gather_tile(const GatherArgs &a, int x, int i, int t,
+                                            const uint8_t **sSrc)
 {
-    __shared__ const uint8_t *sSrc[kMaxTileRows];
-    const int i = blockIdx.y;
-    const int t = blockIdx.z;
     const int r = a.req_ids ? a.req_ids[i] : i;
     int cnt = a.count ? a.count[i] : a.stride;
     cnt = cnt < 0 ? 0 : (cnt > a.stride ? a.stride : cnt);
-    const int j0 = blockIdx.x * a.ts.rows;
+    const int j0 = x * a.ts.rows;
     if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
-        return;
+        return;  // uniform across the workgroup
     const int nrows = min(a.ts.rows, cnt - j0);
     const LayerPtrs lp = a.layers[a.layer[t]];
     const int R = a.sh.R;
@@ -116,24 +119,34 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
     }
 }
 
-// Fill pass: a bounded grid (workers x layers) strides over (request, tile of
-// kFillTile entries) jobs, so the host link is kept busy by a few workers
+template <int MODE>
+__global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
+{
+    __shared__ const uint8_t *sSrc[kMaxTileRows];
+    gather_tile<MODE>(a, blockIdx.x, blockIdx.y, blockIdx.z, sSrc);
+}
+
+// Fill pass: a bounded set of workers (per layer) strides over (request, tile
+// of kFillTile entries) jobs, so the host link is kept busy by a few workers
 // with many loads in flight while the other compute units gather resident
 // rows.  Each job compacts its fresh rows in LDS (their order does not matter:
 // each row has its own two destinations), then streams them.
 constexpr int kFillTile = 1024;
 
-__global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32_t tiles_per_req)
+struct FillList {
+    int32_t row[kFillTile];   // host row (the selection entry's row)
+    int32_t slot[kFillTile];  // hot-cache slot
+    int32_t j[kFillTile];     // selection entry (output row)
+    int32_t n;
+};
+
+__device__ __forceinline__ void fill_jobs(const GatherArgs &a, int t, int worker, int workers,
+                                          int32_t n, int32_t tiles_per_req, FillList &fl)
 {
-    __shared__ const uint8_t *sSrc[kFillTile];
-    __shared__ uint8_t *sHot[kFillTile];
-    __shared__ uint8_t *sOut[kFillTile];
-    __shared__ int sRows;
-    const int t = blockIdx.y;
     const LayerPtrs lp = a.layers[a.layer[t]];
     const int R = a.sh.R;
     const int C = a.ts.chunks;
-    for (int64_t job = blockIdx.x; job < (int64_t)n * tiles_per_req; job += gridDim.x) {
+    for (int64_t job = worker; job < (int64_t)n * tiles_per_req; job += workers) {
         const int i = (int)(job / tiles_per_req);
         const int j0 = (int)(job - (int64_t)i * tiles_per_req) * kFillTile;
         const int r = a.req_ids ? a.req_ids[i] : i;
@@ -142,11 +155,10 @@ __global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32
         if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
             continue;  // uniform across the workgroup
         const int j1 = min(j0 + kFillTile, cnt);
-        __syncthreads();  // the previous job is done with the lists
+        __syncthreads();  // the previous job is done with the list
         if (threadIdx.x == 0)
-            sRows = 0;
+            fl.n = 0;
         __syncthreads();
-        uint8_t *dst = a.out[t] + (int64_t)i * a.stride * R;
         for (int j = j0 + threadIdx.x; j < j1; j += NT) {
             const uint32_t w = a.loc[(int64_t)i * a.stride + j];
             const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
@@ -155,16 +167,19 @@ __global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32
             const uint32_t slot = idx & kSlotMask;
             const int32_t row = a.sel[(int64_t)i * a.stride + j];
             if (slot < (uint32_t)a.sh.B && row >= 0 && (int64_t)row < a.sh.host_rows) {
-                const int k = atomicAdd(&sRows, 1);
-                sSrc[k] = lp.host + ((int64_t)r * a.sh.host_rows + row) * R;
-                sHot[k] = lp.hot + ((int64_t)r * a.sh.B + slot) * R;
-                sOut[k] = dst + (int64_t)j * R;
+                const int k = atomicAdd(&fl.n, 1);
+                fl.row[k] = row;
+                fl.slot[k] = (int32_t)slot;
+                fl.j[k] = j;
             } else if (a.status) {
                 a.status[i] = KVR_E_RANGE;
             }
         }
         __syncthreads();
-        const int total = sRows * C;
+        const uint8_t *src = lp.host + (int64_t)r * a.sh.host_rows * R;
+        uint8_t *hot = lp.hot + (int64_t)r * a.sh.B * R;
+        uint8_t *out = a.out[t] + (int64_t)i * a.stride * R;
+        const int total = fl.n * C;
         for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
             u32x4 v[kUnroll];
             int rr[kUnroll];
@@ -173,17 +188,47 @@ __global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32
                 const int c = c0 + u * NT + threadIdx.x;
                 rr[u] = c < total ? c / C : -1;
                 if (rr[u] >= 0)
-                    load_chunk(v[u], sSrc[rr[u]] + (c - rr[u] * C) * 16);
+                    load_chunk(v[u], src + (int64_t)fl.row[rr[u]] * R + (c - rr[u] * C) * 16);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 if (rr[u] < 0)
                     continue;
                 const int off = (c0 + u * NT + (int)threadIdx.x - rr[u] * C) * 16;
-                store_chunk(sHot[rr[u]] + off, v[u]);
-                store_chunk_nt(sOut[rr[u]] + off, v[u]);
+                store_chunk(hot + (int64_t)fl.slot[rr[u]] * R + off, v[u]);
+                store_chunk_nt(out + (int64_t)fl.j[rr[u]] * R + off, v[u]);
             }
         }
+    }
+}
+
+__global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32_t tiles_per_req)
+{
+    __shared__ FillList fl;
+    fill_jobs(a, blockIdx.y, blockIdx.x, gridDim.x, n, tiles_per_req, fl);
+}
+
+// Fill and resident gather in one 1-D grid: workgroups [0, nt * workers) are
+// the fill workers of every target (so all of them start first), the rest
+// are resident tiles, x fastest, then request entry, then target.
+__global__ __launch_bounds__(NT) void fused_gather_kernel(GatherArgs a, int32_t n,
+                                                          int32_t tiles_per_req, int32_t workers,
+                                                          int32_t nt, int32_t tiles_x)
+{
+    __shared__ union {
+        const uint8_t *src[kMaxTileRows];
+        FillList fill;
+    } sm;
+    const int64_t b = blockIdx.x;
+    const int64_t n_fill = (int64_t)workers * nt;
+    if (b < n_fill) {
+        fill_jobs(a, (int)(b / workers), (int)(b % workers), workers, n, tiles_per_req, sm.fill);
+    } else {
+        const int64_t g = b - n_fill;
+        const int64_t per_t = (int64_t)tiles_x * n;
+        const int t = (int)(g / per_t);
+        const int64_t rem = g - (int64_t)t * per_t;
+        gather_tile<kGatherResident>(a, (int)(rem % tiles_x), (int)(rem / tiles_x), t, sm.src);
     }
 }
 
@@ -210,15 +255,24 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
             a.layer[t] = targets[t0 + t].layer;
             a.out[t] = targets[t0 + t].out;
         }
-        dim3 grid((stride + a.ts.rows - 1) / a.ts.rows, n, nt);
+        const int tiles_x = (stride + a.ts.rows - 1) / a.ts.rows;
+        dim3 grid(tiles_x, n, nt);
+        // fill workers per target: at most one per job
+        const int tiles_per_req = (stride + kFillTile - 1) / kFillTile;
+        const int64_t jobs = (int64_t)n * tiles_per_req;
+        int64_t workers = (kFillWorkers + nt - 1) / nt;
+        workers = workers < jobs ? workers : jobs;
+        workers = workers > 0 ? workers : 1;
         hipError_t e;
         if (mode == kGatherFill) {
-            const int tiles_per_req = (stride + kFillTile - 1) / kFillTile;
-            const int64_t jobs = (int64_t)n * tiles_per_req;
-            int64_t workers = (kFillWorkers + nt - 1) / nt;
-            workers = workers < jobs ? workers : jobs;
-            dim3 fgrid((unsigned)(workers > 0 ? workers : 1), nt);
+            dim3 fgrid((unsigned)workers, nt);
             e = launch(c, KVR_KERNEL_REFILL, fill_kernel, fgrid, dim3(NT), 0, s, a, n, tiles_per_req);
+        } else if (mode == kGatherFused) {
+            const int64_t blocks = workers * nt + (int64_t)tiles_x * n * nt;
+            if (blocks > 0x7FFFFFFF)
+                return hipErrorInvalidConfiguration;
+            e = launch(c, KVR_KERNEL_FUSED, fused_gather_kernel, dim3((unsigned)blocks), dim3(NT), 0,
+                       s, a, n, tiles_per_req, (int32_t)workers, (int32_t)nt, (int32_t)tiles_x);
         } else if (mode == kGatherResident)
             e = launch(c, KVR_KERNEL_GATHER, gather_kernel<kGatherResident>, grid, dim3(NT), 0, s, a);
         else

@@ -416,6 +416,17 @@ int kvr_fill_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, 
                         stride, out, status, stream);
 }
 
+int kvr_fused_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                          const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                          const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                          void *stream)
+{
+    if (n > 0 && stride > 0 && n_layers > 0 && !sel)
+        return fail(KVR_E_ARG, "sel is required");
+    return gather_entry(ctx, kvr::kGatherFused, n_layers, layers, n, req_ids, loc, sel, count,
+                        stride, out, status, stream);
+}
+
 int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,
                                 int32_t *union_rows, int32_t *union_count, int32_t *map,
                                 void *stream)

@@ -128,6 +128,7 @@ struct GatherTarget {
 constexpr int32_t kGatherAll = 0;       // every valid word
 constexpr int32_t kGatherResident = 1;  // every valid word but fresh hot-cache rows
 constexpr int32_t kGatherFill = 2;      // fresh hot-cache rows, from host into slot and out
+constexpr int32_t kGatherFused = 3;     // fill and resident in one launch
 hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *targets,
                          int32_t n_targets, int32_t n, const int32_t *req_ids, const uint32_t *loc,
                          const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,

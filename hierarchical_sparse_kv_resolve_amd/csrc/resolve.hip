@@ -71,6 +71,7 @@ struct ResolveArgs {
     kvr_stats *stats;
     int32_t vc;  // sKey entries: max(NT, next_pow2(min(B, sel_cap)))
     int32_t hs;  // hash entries
+    int32_t bw;  // words of the miss bitmap over rows 0 .. host_rows-1 (0: none)
 };
 
 __device__ __forceinline__ int hslot(int32_t key, int hs)
@@ -191,6 +192,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     uint64_t *sKey = reinterpret_cast<uint64_t *>(lds);
     int32_t *hkey = reinterpret_cast<int32_t *>(sKey + a.vc);
     int32_t *hval = hkey + a.hs;
+    uint32_t *bm = reinterpret_cast<uint32_t *>(hval + a.hs);  // [bw] miss rows
+    int32_t *sChunk = reinterpret_cast<int32_t *>(bm + a.bw);  // [NT] when bw > 0
     __shared__ int sHist[256];
     __shared__ int sCnt[2 * kCntE * NW];  // [kind][e][wave]; e >= EB stays 0
     __shared__ uint32_t sRedU[2 * NW];
@@ -242,6 +245,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         hkey[x] = kEmpty;
         hval[x] = kNoSlot;
     }
+    for (int x = tid; x < a.bw; x += NT)
+        bm[x] = 0;
     for (int x = tid; x < 256; x += NT)
         sHist[x] = 0;
     for (int x = tid; x < 2 * kCntE * NW; x += NT)
@@ -347,7 +352,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     __syncthreads();
 
     // Misses: pending rows no slot holds (each checked once, by the entry that
-    // inserted it); each needs a host copy.  The list packs (row, hash entry).
+    // inserted it); each needs a host copy.  They are marked in the row bitmap
+    // or, without one, listed as packed (row, hash entry).
     uint64_t *sMissList = sKey;
     int32_t hv[EK];
 #pragma unroll
@@ -364,8 +370,13 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         if (lane_id() == 0 && mb)
             wbase = atomicAdd(&sMiss, __popcll(mb));
         wbase = __shfl(wbase, 0, kWave);
-        if (miss)
-            sMissList[wbase + ballot_rank(mb)] = ((uint64_t)(uint32_t)hkey[h] << 32) | h;
+        if (miss) {
+            const int32_t row = hkey[h];
+            if (a.bw > 0)
+                atomicOr(&bm[row >> 5], 1u << (row & 31));
+            else
+                sMissList[wbase + ballot_rank(mb)] = ((uint64_t)(uint32_t)row << 32) | h;
+        }
     }
     __syncthreads();
     if (sHostErr) {
@@ -375,9 +386,41 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     const int m_total = sMiss;
 
     if (m_total > 0) {
-        // Misses in ascending row order (wave-sorted runs merged by rank);
-        // each learns its rank through the hash entry packed with its row.
-        if (m_total <= 256) {
+        // Misses in ascending row order: a miss's rank is the number of miss
+        // rows below it.  With the bitmap, each thread counts the bits of a
+        // run of words, a block scan turns the counts into run offsets, and
+        // each miss adds the bits below it inside its run.  Without it, the
+        // list is sorted (wave-sorted runs merged by rank) and each miss
+        // learns its rank through the hash entry packed with its row.
+        if (a.bw > 0) {
+            const int wpt = (a.bw + NT - 1) / NT;
+            const int w0 = tid * wpt;
+            int cnt = 0;
+            for (int x = w0; x < w0 + wpt && x < a.bw; ++x)
+                cnt += __popc(bm[x]);
+            const int incl = wave_inclusive_scan(cnt);
+            if (lane_id() == kWave - 1)
+                sRedU[wave_id()] = (uint32_t)incl;
+            __syncthreads();
+            int base = 0;
+            for (int w = 0; w < wave_id(); ++w)
+                base += (int)sRedU[w];
+            sChunk[tid] = base + incl - cnt;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                if (!((owned >> e) & 1) || hv[e] != kNoSlot)
+                    continue;
+                const uint32_t h = word[e] & kIndexMask;
+                const int32_t row = hkey[h];
+                const int w = row >> 5;
+                const int c = w / wpt;
+                int rank = sChunk[c] + __popc(bm[w] & ((1u << (row & 31)) - 1u));
+                for (int x = c * wpt; x < w; ++x)
+                    rank += __popc(bm[x]);
+                hval[h] = -1 - rank;
+            }
+        } else if (m_total <= 256) {
             rank_sort_small<NT, uint64_t>(sMissList, m_total);
             for (int q = tid; q < m_total; q += NT)
                 hval[(uint32_t)sMissList[q]] = -1 - q;
@@ -440,12 +483,29 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         if (span > 0) {
             for (int shift = top; shift >= 0; shift -= 8) {
                 const uint32_t hmask = (shift + 8 >= 32) ? 0u : (0xFFFFFFFFu << (shift + 8));
+                if (span < (uint32_t)kWave) {
+                    // one pass over at most 64 stamp values, which candidates
+                    // share in large groups: each wave counts every value by
+                    // ballots and lane v adds value v's count (same-address
+                    // LDS atomics from one wave would be serialized)
+                    int mine = 0;
+                    for (int v = 0; v <= (int)span; ++v) {
+                        int c = 0;
 #pragma unroll
-                for (int e = 0; e < EB; ++e) {
-                    if (cand[e]) {
-                        const uint32_t rel = st[e] - lo;
-                        if ((rel & hmask) == prefix)
-                            atomicAdd(&sHist[(rel >> shift) & 0xFF], 1);
+                        for (int e = 0; e < EB; ++e)
+                            c += __popcll(__ballot(cand[e] && st[e] - lo == (uint32_t)v));
+                        mine = lane_id() == v ? c : mine;
+                    }
+                    if (mine)
+                        atomicAdd(&sHist[lane_id()], mine);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EB; ++e) {
+                        if (cand[e]) {
+                            const uint32_t rel = st[e] - lo;
+                            if ((rel & hmask) == prefix)
+                                atomicAdd(&sHist[(rel >> shift) & 0xFF], 1);
+                        }
                     }
                 }
                 __syncthreads();
@@ -690,30 +750,42 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 
 // Dynamic LDS layout of one resolve workgroup: victim keys then the hash
 // (keys and values).  Returns 0 when the shape does not fit in LDS.
-size_t resolve_lds_layout(const Shape &sh, int32_t *vc, int32_t *hs)
+size_t resolve_lds_layout(const Shape &sh, int32_t *vc, int32_t *hs, int32_t *bw)
 {
     const int m_cap = sh.B < sh.sel_cap ? sh.B : sh.sel_cap;
     const int v = next_pow2(m_cap > NT ? m_cap : NT);
     const size_t budget = kLdsPerCu - kStaticLdsBound;
     if ((size_t)v * 8 >= budget)
         return 0;
-    size_t h = (budget - (size_t)v * 8) / 8;
+    size_t avail = budget - (size_t)v * 8;
+    // keep the hash's load factor at most 0.8 and at least one empty entry
+    const size_t h_min = (size_t)sh.sel_cap + (size_t)sh.sel_cap / 4 + 64;
+    // the miss bitmap (and the scan's run offsets) when it leaves the hash
+    // its minimum
+    const size_t words = (size_t)((sh.host_rows + 31) / 32);
+    const size_t bm_bytes = words * 4 + (size_t)NT * 4;
+    size_t b = 0;
+    if (words > 0 && avail >= bm_bytes + (h_min + 63) / 64 * 64 * 8) {
+        b = words;
+        avail -= bm_bytes;
+    }
+    size_t h = avail / 8;
     const size_t want = (size_t)4 * sh.sel_cap > 256 ? (size_t)4 * sh.sel_cap : 256;
     if (h > want)
         h = want;
     h = h / 64 * 64;
-    // keep the load factor at most 0.8 and at least one empty entry
-    if (h < (size_t)sh.sel_cap + (size_t)sh.sel_cap / 4 + 64)
+    if (h < h_min)
         return 0;
     *vc = v;
     *hs = (int32_t)h;
-    return (size_t)v * 8 + h * 8;
+    *bw = (int32_t)b;
+    return (size_t)v * 8 + h * 8 + (b > 0 ? bm_bytes : 0);
 }
 
 size_t resolve_lds_bytes(const Shape &sh)
 {
-    int32_t vc, hs;
-    return resolve_lds_layout(sh, &vc, &hs);
+    int32_t vc, hs, bw;
+    return resolve_lds_layout(sh, &vc, &hs, &bw);
 }
 
 namespace {
@@ -798,7 +870,7 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
     a.fill_count = fill_count;
     a.status = status;
     a.stats = stats;
-    const size_t lds = resolve_lds_layout(c->shape, &a.vc, &a.hs);
+    const size_t lds = resolve_lds_layout(c->shape, &a.vc, &a.hs, &a.bw);
     return launch(c, KVR_KERNEL_RESOLVE, pick_kernel(c->shape), dim3(n), dim3(NT), lds, s, a);
 }
 

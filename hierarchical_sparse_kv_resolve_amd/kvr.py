@@ -33,7 +33,7 @@ EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
            "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
            "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
-           "kvr_fill_gather_rows", "kvr_residency_create",
+           "kvr_fill_gather_rows", "kvr_fused_gather_rows", "kvr_residency_create",
            "kvr_residency_destroy", "kvr_residency_admit", "kvr_residency_release",
            "kvr_residency_refill", "kvr_residency_counts", "kvr_draft_create",
            "kvr_draft_destroy", "kvr_draft_reset", "kvr_draft_append", "kvr_draft_rollback",
@@ -41,7 +41,7 @@ EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "
            "kvr_staging_acquire", "kvr_staging_release")
 
 # kvr_kernel: kinds of the library's kernel launches (launch timing).
-KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state")
+KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state", "fused")
 
 
 class KvrError(RuntimeError):
@@ -84,6 +84,7 @@ def lib():
             "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_gather_resident_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_fill_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
+            "kvr_fused_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
             "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
             "kvr_reuse_locations": [P, I, I, P, I, P, P, P, P, I, P, P, P, P],
             "kvr_status_summary": [P, I, P],
@@ -240,6 +241,15 @@ class Context:
         _check(lib().kvr_fill_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
                                           _ptr(sel), _ptr(count), stride, arr_o, _ptr(status),
                                           _stream(stream)))
+
+    def fused_gather_rows(self, layers, n, req_ids, loc, sel, count, stride, outs, status=None,
+                          stream=None):
+        nl = len(layers)
+        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
+        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
+        _check(lib().kvr_fused_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
+                                           _ptr(sel), _ptr(count), stride, arr_o, _ptr(status),
+                                           _stream(stream)))
 
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
         _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),

@@ -137,17 +137,21 @@ class GpuRun:
         side stream while the next layer resolves.
 
         fused=True (prefetch_groups is then ignored): the host fill and the
-        gather of fresh rows are one pass (fill_gather_rows, side stream)
-        while every other row is gathered beside it (gather_resident_rows);
-        with one physical source and several resolving layers the resident
-        gathers run on a second side stream, each layer's fill waits for the
-        previous layer's resident gather (its victims may be slots that gather
-        reads) and each resident gather for the previous fill (its hits may be
-        slots that fill wrote).
+        gather of fresh rows are one pass while every other row is gathered
+        beside it.  With distinct payloads both run as one launch on the
+        current stream (fused_gather_rows).  With one physical source and
+        several resolving layers they are two launches: the fill
+        (fill_gather_rows) on a side stream and the resident gathers
+        (gather_resident_rows) on a second side stream; each layer's fill
+        waits for the previous layer's resident gather (its victims may be
+        slots that gather reads) and each resident gather for the previous
+        fill (its hits may be slots that fill wrote).
 
         serialize=True issues the same launches but lets no two of them
         overlap, so launch timing (Context.timing_begin) sees each kernel
-        running alone."""
+        running alone; the fused launch of distinct payloads is then issued
+        as its two halves (fill_gather_rows, then gather_resident_rows), so
+        that each half is timed alone."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
         main = torch.cuda.current_stream()
@@ -167,7 +171,10 @@ class GpuRun:
             fill_layer = -1 if pipelined else 0
             ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
                              self.status[g], self.stats, stream=main)
-            if fused:
+            if fused and cfg.reuse == "distinct" and not serialize:
+                ctx.fused_gather_rows(list(range(self.nl)), n, None, loc, src, count, stride,
+                                      self.outs[g], self.gather_status, stream=main)
+            elif fused:
                 resolved = torch.cuda.Event()
                 resolved.record(main)
                 side = self._side()

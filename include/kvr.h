@@ -225,6 +225,16 @@ int kvr_fill_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, 
                          const int32_t *count, int32_t stride, void *const *out, int32_t *status,
                          void *stream);
 
+/* kvr_fill_gather_rows and kvr_gather_resident_rows as one launch (same
+ * arguments as kvr_fill_gather_rows; writes what the two write together):
+ * part of the grid fills fresh rows from host while the rest gathers the
+ * resident rows, with no wait between two launches on two streams.  Errors as
+ * for the two calls. */
+int kvr_fused_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                          const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                          const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                          void *stream);
+
 /* Verification block dedup ("Speculative state": queries share missing-row
  * retrieval).  Per request: union_rows[i][0..u) = the distinct rows of the q
  * selections, ascending; map[i][qi][j] = index of sel[i][qi][j] in it.
@@ -414,6 +424,7 @@ typedef enum kvr_kernel {
     KVR_KERNEL_GATHER = 3,
     KVR_KERNEL_DEDUP = 4,
     KVR_KERNEL_STATE = 5,    /* state initialisation, location copies */
+    KVR_KERNEL_FUSED = 6,    /* fill pass and resident gather in one launch */
 } kvr_kernel;
 
 int kvr_timing_begin(kvr_ctx *ctx, int32_t capacity);

@@ -261,6 +261,115 @@ def test_gather_alone_random_locations():
     gpu.close()
 
 
+def _fresh_locations(cfg, host_rows, n, stride, seed):
+    """Random words over every place plus fresh hot-cache words: per request
+    distinct fresh slots, every other hot word on a slot that is not fresh
+    (a slot filled in a call is never a hit of the same call)."""
+    rng = np.random.default_rng(seed)
+    loc = np.empty((n, stride), dtype=np.uint32)
+    sel = rng.integers(0, host_rows, (n, stride)).astype(np.int32)
+    for r in range(n):
+        perm = rng.permutation(cfg.B)
+        fresh_slots, other = perm[:cfg.B // 2], perm[cfg.B // 2:]
+        place = rng.integers(0, 3, stride)
+        idx = np.where(place == 0, rng.integers(0, cfg.T, stride),
+                       np.where(place == 1, rng.integers(0, cfg.pool_pages * cfg.P, stride),
+                                other[rng.integers(0, len(other), stride)]))
+        loc[r] = (place.astype(np.uint32) << 30) | idx.astype(np.uint32)
+        pos = rng.choice(stride, len(fresh_slots), replace=False)
+        loc[r, pos] = (2 << 30) | orc.FRESH | fresh_slots.astype(np.uint32)
+        loc[r, rng.integers(0, stride, 5)] = 0xFFFFFFFF
+    return loc, sel
+
+
+def test_fused_gather_alone_equals_two_calls_and_oracle():
+    """kvr_fused_gather_rows against kvr_fill_gather_rows +
+    kvr_gather_resident_rows and against the definition: a fresh word's row
+    is the selection entry's host row, written to its slot and the output;
+    every other valid word is the oracle's gather.  Two fill jobs per request
+    (stride above 1024), ragged and empty counts, invalid words."""
+    import torch
+    cfg = tiny(2).with_(payload_layers=2)
+    inputs = Inputs(cfg)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    try:
+        n, stride = cfg.n_req, 1100
+        loc, sel = _fresh_locations(cfg, inputs.host_rows, n, stride, seed=11)
+        count = np.array([stride, 0, 777], dtype=np.int32)
+        hot0 = [h.clone() for h in gpu.hot]
+        for l in range(2):
+            assert np.array_equal(hot0[l].cpu().numpy(), run.src.hot[l])
+        # the definition, on the CPU
+        exp_out, exp_hot = [], []
+        for l in range(2):
+            fresh = ((loc >> 30) == 2) & (((loc >> 29) & 1) == 1)
+            plain = np.where(fresh, np.uint32(0xFFFFFFFF), loc)
+            out, st = run.src.gather(l, plain, count)
+            assert (st == 0).all()
+            hot = run.src.hot[l].copy()
+            for i in range(n):
+                for j in np.flatnonzero(fresh[i, :count[i]]):
+                    row = run.src.host[l][i, sel[i, j]]
+                    out[i, j] = row
+                    hot[i, loc[i, j] & 0x1FFFFFFF] = row
+            exp_out.append(out)
+            exp_hot.append(hot)
+        loc_d = torch.from_numpy(loc.view(np.int32)).cuda()
+        sel_d = torch.from_numpy(sel).cuda()
+        cnt_d = torch.from_numpy(count).cuda()
+        results = []
+        for path in ("two_calls", "fused"):
+            for l in range(2):
+                gpu.hot[l].copy_(hot0[l])
+            outs = [torch.full((n, stride, cfg.R), 0xEE, dtype=torch.uint8, device="cuda")
+                    for _ in range(2)]
+            st = torch.zeros(n, dtype=torch.int32, device="cuda")
+            if path == "two_calls":
+                gpu.ctx.fill_gather_rows([0, 1], n, None, loc_d, sel_d, cnt_d, stride, outs, st)
+                gpu.ctx.gather_resident_rows([0, 1], n, None, loc_d, cnt_d, stride, outs, st)
+            else:
+                gpu.ctx.fused_gather_rows([0, 1], n, None, loc_d, sel_d, cnt_d, stride, outs, st)
+            torch.cuda.synchronize()
+            assert (st.cpu().numpy() == 0).all(), path
+            for l in range(2):
+                assert np.array_equal(outs[l].cpu().numpy(), exp_out[l]), (path, l)
+                assert np.array_equal(gpu.hot[l].cpu().numpy(), exp_hot[l]), (path, l)
+            results.append(outs)
+        # count = NULL (every entry) and bad words: a fresh slot beyond B, a
+        # host row beyond the store, a page index beyond the pool
+        bad = loc.copy()
+        bad_sel = sel.copy()
+        f0 = np.flatnonzero(((loc[0] >> 29) & 7) == 5)[0]
+        bad[0, f0] = (2 << 30) | orc.FRESH | cfg.B
+        f2 = np.flatnonzero(((loc[2] >> 29) & 7) == 5)[0]
+        bad_sel[2, f2] = inputs.host_rows
+        p1 = np.flatnonzero((loc[1] >> 30) == 1)[0]
+        bad[1, p1] = (1 << 30) | (cfg.pool_pages * cfg.P)
+        statuses = []
+        for path in ("two_calls", "fused"):
+            for l in range(2):
+                gpu.hot[l].copy_(hot0[l])
+            outs = [torch.full((n, stride, cfg.R), 0xEE, dtype=torch.uint8, device="cuda")
+                    for _ in range(2)]
+            st = torch.zeros(n, dtype=torch.int32, device="cuda")
+            args = ([0, 1], n, None, torch.from_numpy(bad.view(np.int32)).cuda(),
+                    torch.from_numpy(bad_sel).cuda(), None, stride, outs, st)
+            if path == "two_calls":
+                gpu.ctx.fill_gather_rows(*args)
+                gpu.ctx.gather_resident_rows(*args[:4], *args[5:])
+            else:
+                gpu.ctx.fused_gather_rows(*args)
+            torch.cuda.synchronize()
+            statuses.append(st.cpu().numpy().tolist())
+            results.append(outs)
+        assert statuses[0] == statuses[1] == [orc.E_RANGE] * 3
+        for l in range(2):
+            assert np.array_equal(results[2][l].cpu().numpy(), results[3][l].cpu().numpy())
+    finally:
+        gpu.close()
+
+
 @pytest.mark.parametrize("q,k", [(1, 1), (4, 90), (3, 1000), (4, 2048), (2, 4096), (5, 0),
                                  (3, 333), (8, 1024)])
 def test_dedup_alone(q, k):
@@ -498,8 +607,8 @@ def test_launch_timing_records_each_kernel():
         gpu.ctx.timing_begin(32)
         gpu.step(3, fused=True)
         rec = gpu.ctx.timing_end()
-        # the fill-and-gather pass is a fill; the resident gather a gather
-        assert [name for name, _ in rec] == ["append", "resolve", "refill", "gather"]
+        # distinct payloads: the fill and the resident gather are one launch
+        assert [name for name, _ in rec] == ["append", "resolve", "fused"]
         compare(run.step(3))
         gpu.ctx.timing_begin(32)
         graph = gpu.capture([3])
@@ -513,6 +622,13 @@ def test_launch_timing_records_each_kernel():
             gpu.ctx.timing_end()
         assert e.value.code == kvr.E_CAPACITY
         compare(run.step(4))
+        gpu.ctx.timing_begin(32)
+        gpu.step(5, fused=True, serialize=True)
+        rec = gpu.ctx.timing_end()
+        # serialized, the fused launch is issued as its two halves: the
+        # fill-and-gather pass (a fill) and the resident gather
+        assert [name for name, _ in rec] == ["append", "resolve", "refill", "gather"]
+        compare(run.step(5))
     finally:
         gpu.close()
 
