@@ -165,10 +165,12 @@ bool tile_magic_exact(int32_t row_bytes)
 {
     Shape sh{};
     sh.R = row_bytes;
-    const TileShape ts = tile_for(sh);
-    for (uint32_t c = 0; c < (uint32_t)(ts.rows * ts.chunks); ++c)
-        if ((uint32_t)(((uint64_t)c * ts.magic) >> 32) != c / (uint32_t)ts.chunks)
-            return false;
+    for (int unroll : {kUnroll, kGatherUnroll}) {
+        const TileShape ts = tile_for(sh, unroll);
+        for (uint32_t c = 0; c < (uint32_t)(ts.rows * ts.chunks); ++c)
+            if ((uint32_t)(((uint64_t)c * ts.magic) >> 32) != c / (uint32_t)ts.chunks)
+                return false;
+    }
     return true;
 }
 
@@ -181,7 +183,7 @@ hipError_t launch_refill(const kvr_ctx *c, const int32_t *layers, int32_t n_laye
 {
     RefillArgs a;
     a.sh = c->shape;
-    a.ts = tile_for(c->shape);
+    a.ts = tile_for(c->shape, kUnroll);
     a.req_ids = req_ids;
     a.fills = fills;
     a.fill_count = fill_count;

@@ -93,11 +93,11 @@ __device__ __forceinline__ void gather_tile(const GatherArgs &a, int x, int i, i
     __syncthreads();
     const int C = a.ts.chunks;
     const int total = nrows * C;
-    for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
-        u32x4 v[kUnroll];
-        int rr[kUnroll];
+    for (int c0 = 0; c0 < total; c0 += NT * kGatherUnroll) {
+        u32x4 v[kGatherUnroll];
+        int rr[kGatherUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kGatherUnroll; ++u) {
             const int c = c0 + u * NT + threadIdx.x;
             rr[u] = -1;
             if (c < total) {
@@ -110,7 +110,7 @@ __device__ __forceinline__ void gather_tile(const GatherArgs &a, int x, int i, i
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kGatherUnroll; ++u) {
             if (rr[u] < 0)
                 continue;
             const int c = c0 + u * NT + threadIdx.x;
@@ -241,7 +241,7 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
 {
     GatherArgs a;
     a.sh = c->shape;
-    a.ts = tile_for(c->shape);
+    a.ts = tile_for(c->shape, kGatherUnroll);
     a.layers = c->layers_d;
     a.req_ids = req_ids;
     a.loc = loc;

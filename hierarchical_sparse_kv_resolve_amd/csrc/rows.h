@@ -17,7 +17,8 @@ namespace kvr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowThreads = 256;  // threads per row-moving workgroup
-constexpr int kUnroll = 8;        // 16-byte loads in flight per lane
+constexpr int kUnroll = 8;        // 16-byte loads in flight per lane (host reads)
+constexpr int kGatherUnroll = 6;  // the same for device gathers: smaller tiles, more of them
 constexpr int kMaxTileRows = 128;
 
 struct TileShape {
@@ -41,13 +42,13 @@ __device__ __forceinline__ void store_chunk(uint8_t *p, const u32x4 &v)
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-// As many whole rows as kUnroll chunks per lane cover, and the multiplier
+// As many whole rows as `unroll` chunks per lane cover, and the multiplier
 // that divides a chunk index by the row's chunk count.
-inline TileShape tile_for(const Shape &sh)
+inline TileShape tile_for(const Shape &sh, int unroll)
 {
     TileShape ts;
     ts.chunks = sh.R / 16;
-    int rows = (kRowThreads * kUnroll) / ts.chunks;
+    int rows = (kRowThreads * unroll) / ts.chunks;
     ts.rows = rows < 1 ? 1 : (rows > kMaxTileRows ? kMaxTileRows : rows);
     ts.magic = (((uint64_t)1 << 32) + ts.chunks - 1) / ts.chunks;
     return ts;
