@@ -315,15 +315,22 @@ int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void 
     return e == hipSuccess ? ok() : hip_fail(e, "append launch");
 }
 
-int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *sel,
-                     const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
-                     int32_t *fill_count, int32_t fill_layer, int32_t *status, kvr_stats *stats,
-                     void *stream)
+static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                         int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
+                         int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
+                         int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream)
 {
     if (int rc = check_ctx(ctx))
         return rc;
     if (int rc = check_n(ctx, n))
         return rc;
+    if (new_rows || append_status) {
+        for (int32_t l = 0; l < ctx->cfg.n_layers; ++l)
+            if (int rc = check_layer(ctx, l))
+                return rc;
+        if (n > 0 && !new_rows)
+            return fail(KVR_E_ARG, "new_rows is required");
+    }
     if (stride < 0 || stride > ctx->cfg.sel_cap)
         return fail(KVR_E_ARG, "stride %d outside [0, sel_cap=%d]", stride, ctx->cfg.sel_cap);
     if (n > 0 && ((stride > 0 && (!sel || !loc)) || !fills || !fill_count || !status))
@@ -337,7 +344,8 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
     if (n == 0)
         return ok();
     hipError_t e = kvr::launch_resolve(ctx, n, req_ids, sel, sel_count, stride, loc, fills,
-                                       fill_count, status, stats, fill_layer >= 0 ? 1 : 0, s);
+                                       fill_count, status, stats, fill_layer >= 0 ? 1 : 0,
+                                       static_cast<const uint8_t *>(new_rows), append_status, s);
     if (e != hipSuccess)
         return hip_fail(e, "resolve launch");
     if (fill_layer >= 0) {
@@ -346,6 +354,26 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
             return hip_fail(e, "refill launch");
     }
     return ok();
+}
+
+int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int32_t *sel,
+                     const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
+                     int32_t *fill_count, int32_t fill_layer, int32_t *status, kvr_stats *stats,
+                     void *stream)
+{
+    return resolve_entry(ctx, n, req_ids, nullptr, nullptr, sel, sel_count, stride, loc, fills,
+                         fill_count, fill_layer, status, stats, stream);
+}
+
+int kvr_append_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                            int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
+                            int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
+                            int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream)
+{
+    if (n > 0 && !new_rows)
+        return fail(KVR_E_ARG, "new_rows is required");
+    return resolve_entry(ctx, n, req_ids, new_rows, append_status, sel, sel_count, stride, loc,
+                         fills, fill_count, fill_layer, status, stats, stream);
 }
 
 static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,

@@ -108,10 +108,13 @@ hipError_t launch(const kvr_ctx *c, int32_t kind, void (*kernel)(P...), dim3 gri
 }
 
 // Launchers (return a hipError_t of the launch).
+// new_rows non-null: the append of kvr_append_rows for the same requests runs
+// first, in the same launch (append_status as its status, may be null).
 hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
                           const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
                           int32_t *fill_count, int32_t *status, kvr_stats *stats,
-                          int32_t count_host_bytes, hipStream_t s);
+                          int32_t count_host_bytes, const uint8_t *new_rows,
+                          int32_t *append_status, hipStream_t s);
 size_t resolve_lds_bytes(const Shape &sh);
 hipError_t prepare_resolve_kernel();
 

@@ -72,6 +72,10 @@ struct ResolveArgs {
     int32_t vc;  // sKey entries: max(NT, next_pow2(min(B, sel_cap)))
     int32_t hs;  // hash entries
     int32_t bw;  // words of the miss bitmap over rows 0 .. host_rows-1 (0: none)
+    // append in the same launch (new_rows non-null): [n_layers][n][R]
+    const LayerPtrs *layers;
+    const uint8_t *new_rows;
+    int32_t *append_status;
 };
 
 __device__ __forceinline__ int hslot(int32_t key, int hs)
@@ -169,6 +173,27 @@ __device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const in
     }
 }
 
+// The request's decoded row of every layer into tail slot L mod T and, written
+// through, host row L (what kvr_append_rows does), by all threads of the block.
+__device__ __forceinline__ void append_row(const ResolveArgs &a, int i, int r, int32_t L)
+{
+    const Shape &sh = a.sh;
+    const int C = sh.R / 16;
+    const int per_layer = C * (sh.T > 0 ? 2 : 1);
+    for (int c = threadIdx.x; c < per_layer * sh.n_layers; c += NT) {
+        const int l = c / per_layer;
+        const int e = c - l * per_layer;
+        const int off = (e % C) * 16;
+        const LayerPtrs lp = a.layers[l];
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(
+            a.new_rows + ((int64_t)l * gridDim.x + i) * sh.R + off);
+        uint8_t *dst = (e < C) ? lp.host + ((int64_t)r * sh.host_rows + L) * sh.R + off
+                               : lp.tail + ((int64_t)r * sh.T + L % sh.T) * sh.R + off;
+        *reinterpret_cast<u32x4 *>(dst) = v;
+    }
+}
+
 __device__ __forceinline__ void fail_request(const ResolveArgs &a, int i, int k, int code)
 {
     uint32_t *loc = a.loc + (int64_t)i * a.stride;
@@ -210,7 +235,32 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     const int hs = a.hs;
     const int r = a.req_ids ? a.req_ids[i] : i;
     int k = a.sel_count ? a.sel_count[i] : a.stride;
-    if (r < 0 || r >= sh.n_req || k < 0 || k > a.stride) {
+    const bool r_ok = r >= 0 && r < sh.n_req;
+    int32_t L = r_ok ? a.L[r] : 0;
+    // Append first when asked (it fails alone, as the separate call would):
+    // every thread has read L before thread 0 publishes L + 1 after a barrier.
+    bool appended = false;
+    if (a.new_rows) {
+        int code = KVR_E_ARG;
+        if (r_ok) {
+            if (L < 0 || (int64_t)L >= sh.host_rows) {
+                code = KVR_E_CAPACITY;
+            } else {
+                append_row(a, i, r, L);
+                appended = true;
+                code = KVR_OK;
+                ++L;
+            }
+        }
+        if (tid == 0 && a.append_status)
+            a.append_status[i] = code;
+    }
+    if (!r_ok || k < 0 || k > a.stride) {
+        if (appended) {
+            __syncthreads();
+            if (tid == 0)
+                a.L[r] = L;
+        }
         fail_request(a, i, k < 0 ? 0 : (k > a.stride ? a.stride : k), KVR_E_ARG);
         return;
     }
@@ -235,7 +285,6 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         t[e] = b < sh.B ? tag[b] : -1;
         st[e] = b < sh.B ? stamp[b] : 0u;
     }
-    const int32_t L = a.L[r];
     const uint32_t clk = a.clock[r];
     const int32_t tail_lo = sh.T > 0 ? max(L - sh.T, 0) : L;
     const int32_t *pmap = a.page_map + (int64_t)r * sh.n_pages;
@@ -259,6 +308,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         sStat = 0;
     }
     __syncthreads();
+    if (appended && tid == 0)
+        a.L[r] = L;
 
     // Step 1 and range check.  Entry e of this thread is selection j = e*NT+tid;
     // its row and location word stay in registers until the end.  Rows in the
@@ -850,9 +901,13 @@ hipError_t prepare_resolve_kernel()
 hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
                           const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
                           int32_t *fill_count, int32_t *status, kvr_stats *stats,
-                          int32_t count_host_bytes, hipStream_t s)
+                          int32_t count_host_bytes, const uint8_t *new_rows,
+                          int32_t *append_status, hipStream_t s)
 {
     ResolveArgs a;
+    a.layers = c->layers_d;
+    a.new_rows = new_rows;
+    a.append_status = append_status;
     a.sh = c->shape;
     a.L = c->L;
     a.page_map = c->page_map;

@@ -29,7 +29,8 @@ REUSE_DISTINCT_PAYLOAD = 1
 
 # Every entry point of include/kvr.h.
 EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
-           "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_gather_rows",
+           "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_append_resolve_rows",
+           "kvr_gather_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
            "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
            "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
@@ -81,6 +82,7 @@ def lib():
             "kvr_init_state": [P, P],
             "kvr_append_rows": [P, I, P, P, P, P],
             "kvr_resolve_rows": [P, I, P, P, P, I, P, P, P, I, P, P, P],
+            "kvr_append_resolve_rows": [P, I, P, P, P, P, P, I, P, P, P, I, P, P, P],
             "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_gather_resident_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_fill_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
@@ -216,6 +218,14 @@ class Context:
         _check(lib().kvr_resolve_rows(self.handle, n, _ptr(req_ids), _ptr(sel), _ptr(sel_count),
                                       stride, _ptr(loc), _ptr(fills), _ptr(fill_count), fill_layer,
                                       _ptr(status), _ptr(stats), _stream(stream)))
+
+    def append_resolve_rows(self, n, req_ids, new_rows, append_status, sel, sel_count, stride, loc,
+                            fills, fill_count, fill_layer, status, stats=None, stream=None):
+        _check(lib().kvr_append_resolve_rows(self.handle, n, _ptr(req_ids), _ptr(new_rows),
+                                             _ptr(append_status), _ptr(sel), _ptr(sel_count),
+                                             stride, _ptr(loc), _ptr(fills), _ptr(fill_count),
+                                             fill_layer, _ptr(status), _ptr(stats),
+                                             _stream(stream)))
 
     def gather_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None, stream=None):
         nl = len(layers)

@@ -40,9 +40,12 @@ def layer_groups(n_layers: int, prefetch_groups) -> list:
 
 
 class GpuRun:
-    def __init__(self, inputs, pool_host=None, device: str = "cuda"):
+    def __init__(self, inputs, pool_host=None, device: str = "cuda", fuse_append: bool = True):
+        """fuse_append: the step's append runs inside its first resolve launch
+        (kvr_append_resolve_rows) instead of as a launch of its own."""
         import torch
         self.torch = torch
+        self.fuse_append = fuse_append
         cfg = inputs.cfg
         self.cfg, self.inputs = cfg, inputs
         dev = torch.device(device)
@@ -156,7 +159,8 @@ class GpuRun:
         cfg, ctx, n = self.cfg, self.ctx, self.n
         main = torch.cuda.current_stream()
         last_filled = last_resident = None
-        ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
+        if not self.fuse_append:
+            ctx.append_rows(n, None, self.rows_dev[s], self.append_status, stream=main)
         for g in range(cfg.groups):
             sel = self.sel_dev[s][g]
             k = sel.shape[-1]
@@ -169,8 +173,13 @@ class GpuRun:
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
             pipelined = bool(prefetch_groups) or fused
             fill_layer = -1 if pipelined else 0
-            ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
-                             self.status[g], self.stats, stream=main)
+            if self.fuse_append and g == 0:
+                ctx.append_resolve_rows(n, None, self.rows_dev[s], self.append_status, src, count,
+                                        stride, loc, fills, fc, fill_layer, self.status[g],
+                                        self.stats, stream=main)
+            else:
+                ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, fill_layer,
+                                 self.status[g], self.stats, stream=main)
             if fused and cfg.reuse == "distinct" and not serialize:
                 ctx.fused_gather_rows(list(range(self.nl)), n, None, loc, src, count, stride,
                                       self.outs[g], self.gather_status, stream=main)

@@ -189,6 +189,18 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
                      int32_t *fill_count, int32_t fill_layer, int32_t *status, kvr_stats *stats,
                      void *stream);
 
+/* kvr_append_rows followed by kvr_resolve_rows for the same requests, in one
+ * launch: each request's row is appended (tail slot L mod T, host row L,
+ * L += 1) before its selection is resolved against the new length.  The
+ * arguments are those of the two calls (new_rows and append_status as in
+ * kvr_append_rows; append_status may be NULL).  An append that fails
+ * (KVR_E_CAPACITY) changes nothing and the resolve still runs, as with the
+ * two calls; an entry whose request id is out of range fails both. */
+int kvr_append_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                            int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
+                            int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
+                            int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream);
+
 /* Gather resolved rows into contiguous per-request buffers, for several
  * payload layers sharing one location vector:
  *   out[l] (device) [n][stride][R] for layers[l]; row j < cnt of request i is

@@ -61,7 +61,8 @@ def _compare_state(gpu, run, reqs):
     assert np.array_equal(st["stamp"][idx], src.stamp)
 
 
-def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0, fused=False):
+def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0, fused=False,
+                fuse_append=True):
     inputs = Inputs(cfg, max_new=max_new)
     reqs = list(range(cfg.n_req)) if reqs is None else list(reqs)
     pool = []
@@ -70,7 +71,7 @@ def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0,
         inputs.fill_pool(l, p)
         pool.append(p)
     print(f"[parity] {cfg.name}: n_req={cfg.n_req} steps={cfg.steps} reqs={len(reqs)}", flush=True)
-    gpu = _gpu_run(inputs, pool_host=pool)
+    gpu = _gpu_run(inputs, pool_host=pool, fuse_append=fuse_append)
     run = OracleRun(inputs, reqs=reqs, pool=pool)
     try:
         for s in range(cfg.steps):
@@ -259,6 +260,85 @@ def test_gather_alone_random_locations():
     torch.cuda.synchronize()
     assert st.cpu().numpy().tolist() == [0, 0, orc.E_RANGE]
     gpu.close()
+
+
+@pytest.mark.parametrize("c", [2, 4, 5])
+def test_separate_append_parity(c):
+    """The step with the append as a launch of its own (kvr_append_rows, then
+    kvr_resolve_rows) instead of inside the first resolve launch."""
+    _run_parity(tiny(c), fuse_append=False)
+    _run_parity(tiny(c), fused=True, fuse_append=False)
+
+
+def test_append_resolve_equals_two_calls():
+    """kvr_append_resolve_rows against kvr_append_rows + kvr_resolve_rows on
+    two copies of one state: a permuted request list, a request already at
+    capacity (its append fails, its resolve still runs), an entry with a
+    selection count beyond the stride (its resolve fails, its append still
+    happens) and a call that also fills layer 0."""
+    import torch
+    cfg = tiny(2).with_(steps=3)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    runs = [_gpu_run(inputs, fuse_append=False), _gpu_run(inputs, fuse_append=False)]
+    try:
+        for g in runs:
+            g.stage(range(cfg.steps))
+            g.L[1] = inputs.host_rows
+        n, k = cfg.n_req, cfg.k
+        perm = [2, 0, 1]
+        req = torch.tensor(perm, dtype=torch.int32, device="cuda")
+        for s in range(cfg.steps):
+            sel = runs[0].sel_dev[s][0][perm].contiguous()
+            count = torch.full((n,), k, dtype=torch.int32, device="cuda")
+            if s == 1:
+                count[1] = k + 1  # entry 1 is request 0
+            fill_layer = 0 if s == 2 else -1
+            outs = []
+            for which, g in enumerate(runs):
+                ast = torch.full((n,), 99, dtype=torch.int32, device="cuda")
+                loc = torch.zeros((n, k), dtype=torch.int32, device="cuda")
+                fills = torch.zeros((n, cfg.B, 2), dtype=torch.int32, device="cuda")
+                fc = torch.zeros(n, dtype=torch.int32, device="cuda")
+                st = torch.zeros(n, dtype=torch.int32, device="cuda")
+                if which == 0:
+                    g.ctx.append_rows(n, req, g.rows_dev[s], ast)
+                    g.ctx.resolve_rows(n, req, sel, count, k, loc, fills, fc, fill_layer, st,
+                                       g.stats)
+                else:
+                    g.ctx.append_resolve_rows(n, req, g.rows_dev[s], ast, sel, count, k, loc,
+                                              fills, fc, fill_layer, st, g.stats)
+                torch.cuda.synchronize()
+                outs.append(dict(ast=ast.cpu().numpy(), loc=loc.cpu().numpy(),
+                                 fills=fills.cpu().numpy(), fc=fc.cpu().numpy(),
+                                 st=st.cpu().numpy(), state=g.state(),
+                                 tail=[t.cpu().numpy() for t in g.tail],
+                                 hot=[h.cpu().numpy() for h in g.hot],
+                                 host=[h.copy() for h in g.host],
+                                 stats=g.stats_dict()))
+            a, b = outs
+            assert a["ast"].tolist() == b["ast"].tolist()
+            assert a["ast"].tolist() == [0, 0, orc.E_CAPACITY]
+            assert a["st"].tolist() == b["st"].tolist()
+            if s == 1:
+                assert a["st"][1] == orc.E_ARG
+            assert np.array_equal(a["fc"], b["fc"])
+            for i in range(n):
+                if a["st"][i] == 0:
+                    assert np.array_equal(a["loc"][i], b["loc"][i])
+                    assert np.array_equal(a["fills"][i, :a["fc"][i]], b["fills"][i, :b["fc"][i]])
+                else:
+                    assert (a["loc"][i, :min(k, int(count[i]))] == -1).all()
+                    assert (b["loc"][i, :min(k, int(count[i]))] == -1).all()
+            for key in ("L", "tag", "stamp", "clock"):
+                assert np.array_equal(a["state"][key], b["state"][key]), key
+            for l in range(cfg.payload_layers):
+                assert np.array_equal(a["tail"][l], b["tail"][l])
+                assert np.array_equal(a["hot"][l], b["hot"][l])
+                assert np.array_equal(a["host"][l], b["host"][l])
+            assert a["stats"] == b["stats"]
+    finally:
+        for g in runs:
+            g.close()
 
 
 def _fresh_locations(cfg, host_rows, n, stride, seed):
@@ -594,21 +674,21 @@ def test_launch_timing_records_each_kernel():
         gpu.ctx.timing_begin(32)
         gpu.step(1)
         rec = gpu.ctx.timing_end()
-        # resolve fills layer 0; one replay call fills layers 1 and 2
-        assert [name for name, _ in rec] == ["append", "resolve", "refill", "refill", "gather"]
+        # append and resolve are one launch; resolve fills layer 0; one replay
+        # call fills layers 1 and 2
+        assert [name for name, _ in rec] == ["resolve", "refill", "refill", "gather"]
         assert all(0.0 < ms < 1000.0 for _, ms in rec)
         compare(run.step(1))
         gpu.ctx.timing_begin(32)
         gpu.step(2, prefetch_groups=2)
         rec = gpu.ctx.timing_end()
-        assert [name for name, _ in rec] == ["append", "resolve", "refill", "refill", "gather",
-                                            "gather"]
+        assert [name for name, _ in rec] == ["resolve", "refill", "refill", "gather", "gather"]
         compare(run.step(2))
         gpu.ctx.timing_begin(32)
         gpu.step(3, fused=True)
         rec = gpu.ctx.timing_end()
         # distinct payloads: the fill and the resident gather are one launch
-        assert [name for name, _ in rec] == ["append", "resolve", "fused"]
+        assert [name for name, _ in rec] == ["resolve", "fused"]
         compare(run.step(3))
         gpu.ctx.timing_begin(32)
         graph = gpu.capture([3])
@@ -627,7 +707,7 @@ def test_launch_timing_records_each_kernel():
         rec = gpu.ctx.timing_end()
         # serialized, the fused launch is issued as its two halves: the
         # fill-and-gather pass (a fill) and the resident gather
-        assert [name for name, _ in rec] == ["append", "resolve", "refill", "gather"]
+        assert [name for name, _ in rec] == ["resolve", "refill", "gather"]
         compare(run.step(5))
     finally:
         gpu.close()
