@@ -450,19 +450,27 @@ def test_fused_gather_alone_equals_two_calls_and_oracle():
         gpu.close()
 
 
+@pytest.mark.parametrize("in_range", [False, True])
 @pytest.mark.parametrize("q,k", [(1, 1), (4, 90), (3, 1000), (4, 2048), (2, 4096), (5, 0),
                                  (3, 333), (8, 1024)])
-def test_dedup_alone(q, k):
+def test_dedup_alone(q, k, in_range):
+    """Against the oracle's dedup.  in_range: rows within the history (the
+    row-bitmap path) except for request 2, which keeps the extreme values
+    (the hash path); otherwise rows anywhere, negative ones included."""
     import torch
     cfg = tiny(4)
     inputs = Inputs(cfg)
     gpu = _gpu_run(inputs)
-    rng = np.random.default_rng(q * 100 + k)
+    rng = np.random.default_rng(q * 100 + k + (7 if in_range else 0))
     n = cfg.n_req
-    sel = rng.integers(-3, 5000, (n, q, k)).astype(np.int32)
+    hi = inputs.host_rows if in_range else 5000
+    sel = rng.integers(0 if in_range else -3, hi, (n, q, k)).astype(np.int32)
     if k:
         sel[0, :, :] = sel[0, 0, 0]          # all equal
         sel[1, -1] = sel[1, 0][::-1]           # a permuted duplicate query
+        if in_range:
+            sel[1, 0, 0] = 0                   # the first and last rows of the bitmap
+            sel[1, -1, -1] = inputs.host_rows - 1
         # extreme values, including the sort's padding value
         flat = sel[2].reshape(-1)
         flat[rng.integers(0, flat.size, 5)] = np.iinfo(np.int32).max
