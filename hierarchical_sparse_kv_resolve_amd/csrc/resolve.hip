@@ -317,9 +317,18 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
     // into the hash once each.
     uint32_t word[EK];
     int owned = 0, nohost = 0, fresh_n = 0;
+    // the page-map entry and the host-copy flag of every entry's page, all
+    // loads issued before any is used
+    int32_t phys[EK];
+    uint8_t hostok[EK];
 #pragma unroll
-    for (int e = 0; e < EK; ++e)
+    for (int e = 0; e < EK; ++e) {
         word[e] = 0;
+        const int32_t p = p_in[e];
+        const bool paged = e * NT + tid < k && p >= 0 && p < tail_lo;
+        phys[e] = paged && p < sh.full_rows ? pmap[p / sh.P] : -1;
+        hostok[e] = paged && p < sh.H ? hvalid[p / sh.P] : (uint8_t)1;
+    }
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
         const int j = e * NT + tid;
@@ -329,19 +338,16 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
                 sRangeErr = 1;
             } else if (p >= tail_lo) {
                 word[e] = (uint32_t)(p % sh.T);
+            } else if (phys[e] >= 0) {
+                word[e] = (1u << kPlaceShift) | (uint32_t)((int64_t)phys[e] * sh.P + p % sh.P);
             } else {
-                const int32_t phys = p < sh.full_rows ? pmap[p / sh.P] : -1;
-                if (phys >= 0) {
-                    word[e] = (1u << kPlaceShift) | (uint32_t)((int64_t)phys * sh.P + p % sh.P);
-                } else {
-                    bool fresh;
-                    word[e] = kPendingTag | (uint32_t)hinsert(hkey, hs, p, fresh);
-                    if (fresh) {
-                        owned |= 1 << e;
-                        ++fresh_n;
-                        if (p < sh.H && !hvalid[p / sh.P])
-                            nohost |= 1 << e;
-                    }
+                bool fresh;
+                word[e] = kPendingTag | (uint32_t)hinsert(hkey, hs, p, fresh);
+                if (fresh) {
+                    owned |= 1 << e;
+                    ++fresh_n;
+                    if (!hostok[e])
+                        nohost |= 1 << e;
                 }
             }
         }
