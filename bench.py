@@ -54,7 +54,8 @@ def parse():
                     help="fused: host fills and the gather of the rows they bring in as one "
                          "pass beside the gather of all other rows; prefetch: fills in layer "
                          "groups ahead of per-group gathers; auto: fused for several payload "
-                         "layers sharing the indices, else prefetch")
+                         "layers sharing the indices or one physical source with several resolving "
+                         "layers (timed eagerly: its graph capture is disabled), else prefetch")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of the K steps from the same state (median reported)")
     ap.add_argument("--hot-slots", type=int, default=0,
@@ -419,13 +420,19 @@ def main():
     pg = args.prefetch_groups
     pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
     # auto: fused where several payload layers share the indices (their
-    # resident gathers are big enough to hide under the fill pass); with one
-    # payload layer the refill in ascending row order reads the host faster
-    fused = args.schedule == "fused" or (args.schedule == "auto" and cfg.reuse == "distinct"
-                                         and cfg.payload_layers > 1)
-    if fused and cfg.reuse != "distinct" and not args.no_graph:
-        raise SystemExit("the fused schedule of one physical source is run eagerly only "
-                         "(--no-graph)")
+    # resident gathers are big enough to hide under the fill pass) or one
+    # physical source serves several resolving layers (each layer's gather
+    # leaves the chain of fills); with one payload layer and one resolve the
+    # refill in ascending row order reads the host faster
+    fused = args.schedule == "fused" or (
+        args.schedule == "auto"
+        and ((cfg.reuse == "distinct" and cfg.payload_layers > 1)
+             or (cfg.reuse != "distinct" and cfg.groups > 1)))
+    no_graph = args.no_graph
+    if fused and cfg.reuse != "distinct" and not no_graph:
+        # its graph capture is disabled (GpuRun.capture): timed eagerly
+        log("the fused schedule of one physical source runs eagerly (no graph)")
+        no_graph = True
     for s in range(W):
         gpu.step(s, prefetch_groups=pg, fused=fused)
     torch.cuda.synchronize()
@@ -441,9 +448,11 @@ def main():
         gpu.step(s, prefetch_groups=pg, serialize=True, fused=fused)
     launches = launch_means_ms(gpu.ctx.timing_end())
     torch.cuda.synchronize()
-    if fused and cfg.reuse == "distinct":
+    if fused:
         # Pass 1b: the timed pass runs the fill and the resident gather as one
-        # launch; time that launch too (eager, one stream, as in the graph).
+        # launch; time that launch too, with the launches of the timed pass
+        # (one stream for distinct payloads; for one physical source each
+        # fused launch overlaps the next layer's resolve, as when timed).
         gpu.restore(snap)
         gpu.ctx.timing_begin(64 * K + 64)
         for s in range(W, total):
@@ -451,7 +460,7 @@ def main():
         fused_runs = launch_means_ms(gpu.ctx.timing_end()).get("fused", [])
         torch.cuda.synchronize()
         launches["fused"] = fused_runs
-    if not args.no_graph:
+    if not no_graph:
         gpu.restore(snap)
         graph = gpu.capture(range(W, total), prefetch_groups=pg, fused=fused)
         torch.cuda.synchronize()
@@ -484,14 +493,14 @@ def main():
 
     walls, gpu_mss = [], []
     for rep in range(max(1, args.repeats)):
-        if rep > 0 or args.no_graph:
+        if rep > 0 or no_graph:
             gpu.restore(snap)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
-        if args.no_graph:
+        if no_graph:
             for s in range(W, total):
                 gpu.step(s, prefetch_groups=pg, fused=fused)
         else:
@@ -538,7 +547,7 @@ def main():
                            + ("; the timed pass runs this gather as the resident part of one "
                               "fused launch with the fill, which is issued here as its two "
                               "halves so that each runs alone"
-                              if fused and cfg.reuse == "distinct" else
+                              if fused else
                               ", with the same launches as the timed pass"))}
 
     found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
@@ -572,7 +581,7 @@ def main():
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": cfg.name, "schedule": "fused" if fused else "prefetch",
                    "prefetch_groups": None if fused else args.prefetch_groups,
-                   "launch": "eager" if args.no_graph else "hip_graph", "n_req": cfg.n_req, "history_rows": cfg.H,
+                   "launch": "eager" if no_graph else "hip_graph", "n_req": cfg.n_req, "history_rows": cfg.H,
                    "row_bytes": cfg.R, "page_rows": cfg.P, "tail_rows": cfg.T,
                    "ready_frac": cfg.ready_frac, "hot_slots": cfg.B, "top_k": cfg.k,
                    "verify_queries": cfg.q, "payload_layers": cfg.payload_layers,

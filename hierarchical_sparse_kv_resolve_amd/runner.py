@@ -141,20 +141,17 @@ class GpuRun:
 
         fused=True (prefetch_groups is then ignored): the host fill and the
         gather of fresh rows are one pass while every other row is gathered
-        beside it.  With distinct payloads both run as one launch on the
-        current stream (fused_gather_rows).  With one physical source and
-        several resolving layers they are two launches: the fill
-        (fill_gather_rows) on a side stream and the resident gathers
-        (gather_resident_rows) on a second side stream; each layer's fill
-        waits for the previous layer's resident gather (its victims may be
-        slots that gather reads) and each resident gather for the previous
-        fill (its hits may be slots that fill wrote).
+        beside it, as one launch (fused_gather_rows): on the current stream
+        with distinct payloads; with one physical source and several
+        resolving layers, on a side stream while the current stream resolves
+        the next layer.
 
-        serialize=True issues the same launches but lets no two of them
+        serialize=True issues the same work but lets no two launches
         overlap, so launch timing (Context.timing_begin) sees each kernel
-        running alone; the fused launch of distinct payloads is then issued
-        as its two halves (fill_gather_rows, then gather_resident_rows), so
-        that each half is timed alone."""
+        running alone; each fused launch is then issued as its two halves
+        (fill_gather_rows, then gather_resident_rows), so that each half is
+        timed alone (for one physical source on two side streams that wait
+        on each other's events)."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
         main = torch.cuda.current_stream()
@@ -183,6 +180,26 @@ class GpuRun:
             if fused and cfg.reuse == "distinct" and not serialize:
                 ctx.fused_gather_rows(list(range(self.nl)), n, None, loc, src, count, stride,
                                       self.outs[g], self.gather_status, stream=main)
+            elif fused and not serialize:
+                # One physical source: each layer's fused launch runs on the
+                # side stream while the main stream resolves the next layer
+                # (resolve touches metadata only); on one stream the next
+                # layer's fill comes after this layer's resident gather (its
+                # victims may be slots that gather reads) and its resident
+                # gather after this fill (its hits may be slots the fill wrote).
+                resolved = torch.cuda.Event()
+                resolved.record(main)
+                side = self._side()
+                side.wait_event(resolved)
+                ctx.fused_gather_rows([0], n, None, loc, src, count, stride, self.outs[g][:1],
+                                      self.gather_status, stream=side)
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=main)
+                if g == cfg.groups - 1:
+                    done = torch.cuda.Event()
+                    done.record(side)
+                    main.wait_event(done)
             elif fused:
                 resolved = torch.cuda.Event()
                 resolved.record(main)
@@ -320,10 +337,12 @@ class GpuRun:
         whatever state the buffers hold."""
         torch = self.torch
         if fused and self.cfg.reuse != "distinct":
-            # Capturing this schedule (two side streams that wait on each
-            # other's events across resolving layers) ended in a host crash
-            # inside the graph runtime's capture end; until a cause is shown it
-            # is not captured.  The eager schedule is unaffected.
+            # Capturing this schedule in an earlier form (the fill and the
+            # resident gathers as two launches on two side streams that waited
+            # on each other's events across resolving layers) ended in a host
+            # crash inside the graph runtime's capture end.  No cause was
+            # found, so this schedule is not captured in any form; eager runs
+            # are unaffected.
             raise NotImplementedError("graph capture of the fused schedule for one physical "
                                       "source with several resolving layers is disabled")
         graph = torch.cuda.CUDAGraph()

@@ -58,6 +58,22 @@ def test_null_context_and_status_summary():
     assert lib.kvr_destroy(None) == kvr.OK
 
 
+def test_hot_path_calls_reject_a_null_context():
+    lib = kvr.lib()
+    layers = (ctypes.c_int32 * 1)(0)
+    outs = (ctypes.c_void_p * 1)(None)
+    assert lib.kvr_append_resolve_rows(None, 0, None, None, None, None, None, 0, None, None, None,
+                                       -1, None, None, None) == kvr.E_ARG
+    assert lib.kvr_append_rows(None, 0, None, None, None, None) == kvr.E_ARG
+    for name in ("kvr_gather_rows", "kvr_gather_resident_rows"):
+        assert getattr(lib, name)(None, 1, layers, 0, None, None, None, 0, outs, None,
+                                  None) == kvr.E_ARG
+    for name in ("kvr_fill_gather_rows", "kvr_fused_gather_rows"):
+        assert getattr(lib, name)(None, 1, layers, 0, None, None, None, None, 0, outs, None,
+                                  None) == kvr.E_ARG
+        assert "null context" in kvr.last_error()
+
+
 def test_kernel_kinds_match_the_binding():
     text = open(os.path.join(ROOT, "include", "kvr.h")).read()
     kinds = {name.lower(): int(v) for name, v in re.findall(r"KVR_KERNEL_([A-Z]+)\s*=\s*(\d+)", text)}

@@ -341,6 +341,42 @@ def test_append_resolve_equals_two_calls():
             g.close()
 
 
+def test_fused_entry_points_reject_missing_arguments():
+    """Argument errors of the fused entry points return synchronously and
+    launch nothing."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2)
+    inputs = Inputs(cfg)
+    gpu = _gpu_run(inputs)
+    try:
+        n, k = cfg.n_req, cfg.k
+        loc = torch.zeros((n, k), dtype=torch.int32, device="cuda")
+        outs = [torch.zeros((n, k, cfg.R), dtype=torch.uint8, device="cuda")]
+        with pytest.raises(kvr.KvrError) as e:
+            gpu.ctx.fused_gather_rows([0], n, None, loc, None, None, k, outs)
+        assert e.value.code == kvr.E_ARG and "sel" in str(e.value)
+        with pytest.raises(kvr.KvrError) as e:
+            gpu.ctx.fused_gather_rows([cfg.payload_layers], n, None, loc, loc, None, k, outs)
+        assert e.value.code == kvr.E_ARG
+        sel = torch.zeros((n, k), dtype=torch.int32, device="cuda")
+        fills = torch.zeros((n, cfg.B, 2), dtype=torch.int32, device="cuda")
+        fc = torch.zeros(n, dtype=torch.int32, device="cuda")
+        st = torch.zeros(n, dtype=torch.int32, device="cuda")
+        with pytest.raises(kvr.KvrError) as e:
+            gpu.ctx.append_resolve_rows(n, None, None, None, sel, None, k, loc, fills, fc, -1, st)
+        assert e.value.code == kvr.E_ARG and "new_rows" in str(e.value)
+        with pytest.raises(kvr.KvrError) as e:
+            gpu.ctx.append_resolve_rows(n, None, sel, None, sel, None, cfg.sel_cap + 1, loc,
+                                        fills, fc, -1, st)
+        assert e.value.code == kvr.E_ARG and "stride" in str(e.value)
+        torch.cuda.synchronize()
+        st0 = gpu.state()
+        assert (st0["L"] == cfg.H).all()  # nothing ran
+    finally:
+        gpu.close()
+
+
 def _fresh_locations(cfg, host_rows, n, stride, seed):
     """Random words over every place plus fresh hot-cache words: per request
     distinct fresh slots, every other hot word on a slot that is not fresh
