@@ -644,9 +644,10 @@ def test_closed_form_bytes_full_glm_shape():
 # ------------------------------------------------------------------ HIP graphs
 
 
-_CAPTURE_CRASH = ("capturing the fused schedule for one physical source (two side streams "
-                  "waiting on each other's events) crashed the host in the graph runtime's "
-                  "capture end; disabled until a cause is shown")
+_CAPTURE_CRASH = ("capturing the fused schedule for one physical source (in an earlier form "
+                  "with two side streams waiting on each other's events) crashed the host in "
+                  "the graph runtime's capture end; capture of this schedule stays disabled "
+                  "until a cause is shown")
 
 
 @pytest.mark.parametrize("shape,prefetch_groups,fused", [
