@@ -197,6 +197,30 @@ def test_hot_budget_parity_full_size(c, B, reqs):
     _run_parity(FULL[c].with_(B=B, steps=6), reqs=reqs, check_hot=False)
 
 
+@pytest.mark.parametrize("seed", range(9))
+def test_random_shapes_parity(seed):
+    """Seeded random reduced shapes (history, page and tail sizes, budgets
+    from tight to roomy, row sizes, request, layer and group counts, verify
+    blocks) on the one-stream, fused and prefetch schedules."""
+    rng = np.random.default_rng(1000 + seed)
+    base = tiny([2, 4, 5][seed % 3])
+    H = int(rng.integers(200, 3000))
+    k = int(rng.integers(1, min(300, H // 4)))
+    kw = dict(name=f"rand{seed}", n_req=int(rng.integers(1, 5)), H=H,
+              P=int(rng.choice([1, 7, 16, 64])), T=int(rng.choice([0, 3, 40, 129])), k=k,
+              B=int(rng.integers(max(1, k // 2), 2 * k + 40)),
+              R=int(rng.choice([16, 48, 656, 1152])), steps=4,
+              ready_frac=float(rng.choice([0.0, 0.3, 1.0])), seed=5000 + seed)
+    if base.reuse == "distinct":
+        kw["payload_layers"] = int(rng.integers(1, 4))
+    else:
+        kw["groups"] = int(rng.integers(1, 4))
+    cfg = base.with_(**kw)
+    print(f"[parity] random shape {cfg}", flush=True)
+    for sched in (dict(), dict(fused=True), dict(prefetch_groups=2)):
+        _run_parity(cfg, **sched)
+
+
 def test_prefetch_group_sizes_parity():
     """Explicit, unequal layer groups for the host fills and gathers."""
     _run_parity(tiny(2), prefetch_groups=(2, 1))
