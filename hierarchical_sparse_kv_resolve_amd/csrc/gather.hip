@@ -30,7 +30,7 @@ constexpr int NT = kRowThreads;
 // Fill workers per launch, over all its layers (at most one per job): enough
 // jobs in flight to keep the host link busy, few enough that the resident
 // gather running beside them keeps its compute units.
-constexpr int kFillWorkers = 512;
+constexpr int kFillWorkers = 256;
 
 struct GatherArgs {
     Shape sh;
