@@ -2,7 +2,8 @@
 // hot-cache slots (also the per-layer replay for shared indices with distinct
 // payloads), the tail append, and small state kernels.  Host rows are read
 // straight from pinned memory through its device mapping (zero copy over the
-// host link), in the same tiles of whole rows as the gather.
+// host link), in tiles of whole rows like the gather's (sized for more loads
+// in flight per lane, as host reads wait longer).
 #include "kvr_internal.h"
 #include "rows.h"
 

@@ -5,7 +5,9 @@
 // is taken from the tail or a ready optional-history page if it is there,
 // else from the B-slot hot cache (with LRU stamps), else it is copied from
 // pinned host memory into an LRU victim slot.  The host copy itself is done
-// by the refill kernel (copy.hip) from the fill list written here.
+// by the refill or fill kernels (copy.hip, gather.hip) from the fill list or
+// the location words written here.  On request the same launch first appends
+// each request's decoded row (the tail write of "Memory split").
 //
 // One workgroup of 1024 threads (16 waves) owns one request for the whole
 // call, so every decision about that request's hot cache is made in one place
@@ -14,21 +16,25 @@
 //              if absent dedups them; each thread keeps the entries of its
 //              selection entries in registers); hval holds the row's hot
 //              slot, the rank of the miss, or the filled slot,
-//   sKey       the misses in ascending row order and then the victims'
-//              (stamp << 32 | slot) keys in victim order.
+//   bm         a bitmap over the request's rows marking the misses (when it
+//              fits beside the hash): a miss's rank is the number of set
+//              bits below it, from a block scan of the words' popcounts,
+//   sKey       the victims' (stamp << 32 | slot) keys in victim order (and,
+//              without the bitmap, first the misses to be sorted).
 // The hot-cache scan looks each of the B tags up once in the hash, so the
 // work per call is bounded by B and by the selection size, never by the
 // history length.  Tags and stamps are loaded at kernel start so their
 // latency hides behind step 1.
 //
 // Victims are the m smallest (stamp, slot) keys among the slots not hit in the
-// call.  A radix select over stamp digits finds the threshold stamp tau;
-// every candidate older than tau is a victim, and the youngest victims are
-// the first candidates stamped tau in slot order (ordered compaction with
-// wave ballots).  Only the candidates older than tau are sorted, and only
-// when their stamps differ.  Misses take victims in ascending row order.
-// Up to 256 keys are put in order by counting ranks; more by sorting a run
-// per wave in registers and merging the runs by rank (block_merge_sort).
+// call.  A radix select over stamp digits finds the threshold stamp tau (when
+// all stamps lie within 64 values, by ballot counts per value); every
+// candidate older than tau is a victim, and the youngest victims are the
+// first candidates stamped tau in slot order (ordered compaction with wave
+// ballots).  Only the candidates older than tau are sorted, and only when
+// their stamps differ.  Misses take victims in ascending row order.  Up to
+// 256 keys are put in order by counting ranks; more by sorting a run per wave
+// in registers and merging the runs by rank (block_merge_sort).
 #include <climits>
 
 #include "block.h"
