@@ -221,6 +221,18 @@ def test_random_shapes_parity(seed):
         _run_parity(cfg, **sched)
 
 
+@pytest.mark.parametrize("c,kw", [(2, dict(k=600)), (2, dict(k=200)), (4, dict(k=300, q=2))])
+def test_long_history_parity(c, kw):
+    """Histories of 1.3 M rows (16-byte rows keep the stores small): too long
+    for the row bitmaps beside the resolve's hash and in the dedup's LDS, so
+    misses are ranked by sorting (counting ranks up to 256 misses per call,
+    the merge sort above) and the verify union by the hash path."""
+    cfg = tiny(c).with_(name="long_history", H=1_300_000, R=16, n_req=2, B=1500, T=16, P=64,
+                        ready_frac=0.0, steps=4, payload_layers=1, **kw)
+    _run_parity(cfg)
+    _run_parity(cfg, fused=True)
+
+
 def test_prefetch_group_sizes_parity():
     """Explicit, unequal layer groups for the host fills and gathers."""
     _run_parity(tiny(2), prefetch_groups=(2, 1))
