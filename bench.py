@@ -54,8 +54,9 @@ def parse():
                     help="fused: host fills and the gather of the rows they bring in as one "
                          "pass beside the gather of all other rows; prefetch: fills in layer "
                          "groups ahead of per-group gathers; auto: fused for several payload "
-                         "layers sharing the indices or one physical source with several resolving "
-                         "layers (timed eagerly: its graph capture is disabled), else prefetch")
+                         "layers sharing the indices, one physical source with several resolving "
+                         "layers (timed eagerly: its graph capture is disabled) or small calls "
+                         "(n_req * sel_cap <= 4096), else prefetch")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of the K steps from the same state (median reported)")
     ap.add_argument("--hot-slots", type=int, default=0,
@@ -423,11 +424,13 @@ def main():
     # resident gathers are big enough to hide under the fill pass) or one
     # physical source serves several resolving layers (each layer's gather
     # leaves the chain of fills); with one payload layer and one resolve the
-    # refill in ascending row order reads the host faster
+    # refill in ascending row order reads the host faster, unless the call
+    # is so small that latency rules (a launch fewer then counts most)
     fused = args.schedule == "fused" or (
         args.schedule == "auto"
         and ((cfg.reuse == "distinct" and cfg.payload_layers > 1)
-             or (cfg.reuse != "distinct" and cfg.groups > 1)))
+             or (cfg.reuse != "distinct" and cfg.groups > 1)
+             or cfg.n_req * cfg.sel_cap <= 4096))
     no_graph = args.no_graph
     if fused and cfg.reuse != "distinct" and not no_graph:
         # its graph capture is disabled (GpuRun.capture): timed eagerly

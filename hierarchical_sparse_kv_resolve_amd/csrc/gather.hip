@@ -44,6 +44,7 @@ struct GatherArgs {
     const int32_t *sel;       // [n][stride] the resolved selection (fill mode)
     int32_t stride;
     int32_t *status;
+    int32_t fill_tile;        // entries per fill job (at most kFillTile)
 };
 
 // Source of a word in the all and resident modes (null: nothing to copy).
@@ -127,11 +128,16 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 }
 
 // Fill pass: a bounded set of workers (per layer) strides over (request, tile
-// of kFillTile entries) jobs, so the host link is kept busy by a few workers
+// of fill_tile entries) jobs, so the host link is kept busy by a few workers
 // with many loads in flight while the other compute units gather resident
 // rows.  Each job compacts its fresh rows in LDS (their order does not matter:
-// each row has its own two destinations), then streams them.
+// each row has its own two destinations), then streams them.  Jobs take 1024
+// entries, or fewer when a call has fewer than 16 such jobs' worth of entries
+// per layer (down to 16 entries), so that a small call still has 16 workers
+// per layer drawing on the host link.
 constexpr int kFillTile = 1024;
+constexpr int kFillTileMin = 16;
+constexpr int kFillJobsMin = 16;
 
 struct FillList {
     int32_t row[kFillTile];   // host row (the selection entry's row)
@@ -148,13 +154,13 @@ __device__ __forceinline__ void fill_jobs(const GatherArgs &a, int t, int worker
     const int C = a.ts.chunks;
     for (int64_t job = worker; job < (int64_t)n * tiles_per_req; job += workers) {
         const int i = (int)(job / tiles_per_req);
-        const int j0 = (int)(job - (int64_t)i * tiles_per_req) * kFillTile;
+        const int j0 = (int)(job - (int64_t)i * tiles_per_req) * a.fill_tile;
         const int r = a.req_ids ? a.req_ids[i] : i;
         int cnt = a.count ? a.count[i] : a.stride;
         cnt = cnt < 0 ? 0 : (cnt > a.stride ? a.stride : cnt);
         if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
             continue;  // uniform across the workgroup
-        const int j1 = min(j0 + kFillTile, cnt);
+        const int j1 = min(j0 + a.fill_tile, cnt);
         __syncthreads();  // the previous job is done with the list
         if (threadIdx.x == 0)
             fl.n = 0;
@@ -258,7 +264,11 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
         const int tiles_x = (stride + a.ts.rows - 1) / a.ts.rows;
         dim3 grid(tiles_x, n, nt);
         // fill workers per target: at most one per job
-        const int tiles_per_req = (stride + kFillTile - 1) / kFillTile;
+        int ft = kFillTileMin;
+        while (ft < kFillTile && (int64_t)ft * kFillJobsMin < (int64_t)n * stride)
+            ft *= 2;
+        a.fill_tile = ft;
+        const int tiles_per_req = (stride + ft - 1) / ft;
         const int64_t jobs = (int64_t)n * tiles_per_req;
         int64_t workers = (kFillWorkers + nt - 1) / nt;
         workers = workers < jobs ? workers : jobs;
