@@ -136,6 +136,7 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 // per layer (down to 16 entries), so that a small call still has 16 workers
 // per layer drawing on the host link.
 constexpr int kFillTile = 1024;
+constexpr int kFillPer = kFillTile / NT;  // entries per thread of a full job
 constexpr int kFillTileMin = 16;
 constexpr int kFillJobsMin = 16;
 
@@ -161,22 +162,34 @@ __device__ __forceinline__ void fill_jobs(const GatherArgs &a, int t, int worker
         if (j0 >= cnt || r < 0 || r >= a.sh.n_req)
             continue;  // uniform across the workgroup
         const int j1 = min(j0 + a.fill_tile, cnt);
+        // every location word and selection row of the job is loaded before
+        // any is used (one memory round trip, not one per pass), and before
+        // the barriers, which it overlaps
+        uint32_t wv[kFillPer];
+        int32_t rv[kFillPer];
+#pragma unroll
+        for (int u = 0; u < kFillPer; ++u) {
+            const int j = j0 + u * NT + (int)threadIdx.x;
+            wv[u] = j < j1 ? a.loc[(int64_t)i * a.stride + j] : KVR_LOC_INVALID;
+            rv[u] = j < j1 ? a.sel[(int64_t)i * a.stride + j] : -1;
+        }
         __syncthreads();  // the previous job is done with the list
         if (threadIdx.x == 0)
             fl.n = 0;
         __syncthreads();
-        for (int j = j0 + threadIdx.x; j < j1; j += NT) {
-            const uint32_t w = a.loc[(int64_t)i * a.stride + j];
+#pragma unroll
+        for (int u = 0; u < kFillPer; ++u) {
+            const uint32_t w = wv[u];
             const uint32_t place = w >> kPlaceShift, idx = w & kIndexMask;
             if (w == KVR_LOC_INVALID || place != KVR_PLACE_HOT || !(idx & kFreshBit))
                 continue;
             const uint32_t slot = idx & kSlotMask;
-            const int32_t row = a.sel[(int64_t)i * a.stride + j];
+            const int32_t row = rv[u];
             if (slot < (uint32_t)a.sh.B && row >= 0 && (int64_t)row < a.sh.host_rows) {
                 const int k = atomicAdd(&fl.n, 1);
                 fl.row[k] = row;
                 fl.slot[k] = (int32_t)slot;
-                fl.j[k] = j;
+                fl.j[k] = j0 + u * NT + (int)threadIdx.x;
             } else if (a.status) {
                 a.status[i] = KVR_E_RANGE;
             }
