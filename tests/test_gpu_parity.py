@@ -233,6 +233,14 @@ def test_long_history_parity(c, kw):
     _run_parity(cfg, fused=True)
 
 
+def test_more_layers_than_one_launch_takes():
+    """26 payload layers sharing the indices: the gathers, replays and fused
+    fill-and-gather calls split into launches of at most 24 layers."""
+    cfg = tiny(2).with_(name="many_layers", payload_layers=26, R=16, steps=3)
+    for sched in (dict(), dict(fused=True), dict(prefetch_groups=2)):
+        _run_parity(cfg, **sched)
+
+
 def test_prefetch_group_sizes_parity():
     """Explicit, unequal layer groups for the host fills and gathers."""
     _run_parity(tiny(2), prefetch_groups=(2, 1))
