@@ -2,9 +2,10 @@
 
 Owns the device buffers (torch allocates them; pinned host stores come from
 kvr_host_alloc), binds them to a libkvr context and issues, per decode step,
-stream-ordered calls with no host synchronisation:
+stream-ordered calls with no host synchronisation.  The one-stream schedule:
 
-  append one decoded row per request (all payload layers)
+  append one decoded row per request (all payload layers; by default inside
+  the first resolve launch: append_resolve_rows)
   for each resolving layer, in order:
       [verify block]  dedup_verify_selections -> union
       resolve_rows    (tail / ready page / hot scan / LRU victims; host refill
@@ -15,6 +16,10 @@ stream-ordered calls with no host synchronisation:
       one physical source: gather_rows of the source, then
                        reuse_locations(SHARED_SOURCE) for each Reuse layer
                        (an alias: no bytes move)
+
+The prefetch and fused schedules (GpuRun.step) reorder the fills and gathers
+of the same calls; the fused one fills from host and gathers in one launch
+(fused_gather_rows).
 
 `inputs` supplies shapes and seeded contents (cfg, page_map, host_valid,
 fill_tail/fill_pool/fill_host, new_rows, selections).

@@ -1,0 +1,48 @@
+"""Host-side helpers of bench.py (CPU only): the recorded traffic is used only
+for the workload, schedule and gather source it was measured on; launch
+records group by kernel; layer groups split the payload layers."""
+from __future__ import annotations
+
+import re
+
+import numpy as np
+import pytest
+
+import bench
+from hierarchical_sparse_kv_resolve_amd.runner import layer_groups
+
+
+def test_recorded_traffic_matches_workload_schedule_and_source():
+    text = open(bench.TRAFFIC_PROFILE).read()
+    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
+    wl, sched = fields["workload"], fields["schedule"]
+    if fields["source_sha256"] == bench.gather_source_hash():
+        assert bench.recorded_traffic(wl, sched) == int(fields["traffic_bytes_per_launch"])
+    else:  # the gather source changed since the counters were taken
+        assert bench.recorded_traffic(wl, sched) is None
+    assert bench.recorded_traffic(wl, "prefetch:2") is None
+    assert bench.recorded_traffic("c4_speculative_verify", sched) is None
+
+
+def test_launch_means_group_by_kernel():
+    recs = [("resolve", 0.02), ("fused", 0.2), ("resolve", 0.03)]
+    assert bench.launch_means_ms(recs) == {"resolve": [0.02, 0.03], "fused": [0.2]}
+
+
+@pytest.mark.parametrize("n,g,sizes", [(8, 2, [4, 4]), (8, 3, [3, 3, 2]), (1, 2, [1]),
+                                       (5, (2, 3), [2, 3])])
+def test_layer_groups(n, g, sizes):
+    groups = layer_groups(n, g)
+    assert [len(x) for x in groups] == sizes
+    assert np.array_equal(np.concatenate(groups), np.arange(n))
+
+
+def test_layer_groups_reject_bad_sizes():
+    with pytest.raises(ValueError):
+        layer_groups(4, (2, 1))
+    with pytest.raises(ValueError):
+        layer_groups(4, (4, 0))
+
+
+def test_cpu_model_is_a_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
