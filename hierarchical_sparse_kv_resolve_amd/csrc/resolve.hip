@@ -551,12 +551,18 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
                     // share in large groups: each wave counts every value by
                     // ballots and lane v adds value v's count (same-address
                     // LDS atomics from one wave would be serialized)
+                    // (non-candidates compare as a value above any v)
+                    uint32_t rel[EB];
+#pragma unroll
+                    for (int e = 0; e < EB; ++e)
+                        rel[e] = cand[e] ? st[e] - lo : 0xFFFFFFFFu;
                     int mine = 0;
-                    for (int v = 0; v <= (int)span; ++v) {
+                    const int vmax = __builtin_amdgcn_readfirstlane((int)span);  // uniform
+                    for (int v = 0; v <= vmax; ++v) {
                         int c = 0;
 #pragma unroll
                         for (int e = 0; e < EB; ++e)
-                            c += __popcll(__ballot(cand[e] && st[e] - lo == (uint32_t)v));
+                            c += __popcll(__builtin_amdgcn_uicmp(rel[e], (uint32_t)v, 32));  // ==
                         mine = lane_id() == v ? c : mine;
                     }
                     if (mine)
