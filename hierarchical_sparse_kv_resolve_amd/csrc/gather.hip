@@ -30,7 +30,7 @@ constexpr int NT = kRowThreads;
 // Fill workers per launch, over all its layers (at most one per job): enough
 // jobs in flight to keep the host link busy, few enough that the resident
 // gather running beside them keeps its compute units.
-constexpr int kFillWorkers = 256;
+constexpr int kFillWorkers = 128;
 
 struct GatherArgs {
     Shape sh;
@@ -153,9 +153,13 @@ __device__ __forceinline__ void fill_jobs(const GatherArgs &a, int t, int worker
     const LayerPtrs lp = a.layers[a.layer[t]];
     const int R = a.sh.R;
     const int C = a.ts.chunks;
+    // jobs in tile-major order: a worker's jobs (worker, worker + workers, ...)
+    // spread over tiles, so that when counts fall short of the stride (a
+    // verify union) the empty last tiles do not all land on the same workers
     for (int64_t job = worker; job < (int64_t)n * tiles_per_req; job += workers) {
-        const int i = (int)(job / tiles_per_req);
-        const int j0 = (int)(job - (int64_t)i * tiles_per_req) * a.fill_tile;
+        const int tile = (int)(job / n);
+        const int i = (int)(job - (int64_t)tile * n);
+        const int j0 = tile * a.fill_tile;
         const int r = a.req_ids ? a.req_ids[i] : i;
         int cnt = a.count ? a.count[i] : a.stride;
         cnt = cnt < 0 ? 0 : (cnt > a.stride ? a.stride : cnt);
