@@ -195,7 +195,9 @@ int kvr_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int3
  * arguments are those of the two calls (new_rows and append_status as in
  * kvr_append_rows; append_status may be NULL).  An append that fails
  * (KVR_E_CAPACITY) changes nothing and the resolve still runs, as with the
- * two calls; an entry whose request id is out of range fails both. */
+ * two calls; an entry whose request id is out of range fails both; one whose
+ * selection count is out of range fails its resolve (KVR_E_ARG) after its
+ * append. */
 int kvr_append_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
                             int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
                             int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
