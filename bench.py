@@ -391,7 +391,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the resolver keeps each request's state on "
-              "one device and this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+              "one device and the library has no multi-GPU path (--gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
