@@ -6,7 +6,7 @@
 // pool or hot cache.  One launch serves every payload layer that shares the
 // location vector (grid z = layer).
 //
-// Three modes of one kernel:
+// Modes (the first two of one kernel):
 //   all       every valid word (fresh hot-cache rows read from their slots);
 //   resident  every valid word except fresh hot-cache rows; it reads no slot
 //             a fill of the same call writes, so it runs beside the fills;
