@@ -171,7 +171,7 @@ def host_link_gbs(torch, nbytes=1 << 30, reps=5):
 # Counter-based HBM traffic of the gather kernel on the shared-indices GLM
 # workload.  The summary records the hash of the kernel source it was taken
 # with; once the source changes the figure no longer applies and is dropped.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gather_kernel_glm_traffic.md")
+TRAFFIC_PROFILES = os.path.join(ROOT, "profiles", "gather_kernel_*_traffic.md")
 GATHER_SOURCES = [os.path.join(ROOT, "hierarchical_sparse_kv_resolve_amd", "csrc", name)
                   for name in ("gather.hip", "rows.h")]
 
@@ -186,21 +186,28 @@ def gather_source_hash():
     return h.hexdigest()
 
 
+def traffic_records():
+    """The recorded counter summaries: one dict of fields per profile file."""
+    import glob
+    out = []
+    for path in sorted(glob.glob(TRAFFIC_PROFILES)):
+        with open(path) as f:
+            out.append(dict(re.findall(r"^(\w+): (\S+)$", f.read(), re.M)))
+    return out
+
+
 def recorded_traffic(workload, schedule):
-    """HBM bytes per gather launch measured by counters, or None."""
-    try:
-        with open(TRAFFIC_PROFILE) as f:
-            text = f.read()
-    except OSError:
-        return None
-    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
-    if (fields.get("workload") != workload or fields.get("schedule") != schedule
-            or fields.get("source_sha256") != gather_source_hash()):
-        return None
-    try:
-        return int(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    """HBM bytes per gather launch measured by counters for this workload and
+    schedule on the current gather source, or None."""
+    source = gather_source_hash()
+    for fields in traffic_records():
+        if (fields.get("workload") == workload and fields.get("schedule") == schedule
+                and fields.get("source_sha256") == source):
+            try:
+                return int(fields["traffic_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=3):

@@ -3,8 +3,6 @@ for the workload, schedule and gather source it was measured on; launch
 records group by kernel; layer groups split the payload layers."""
 from __future__ import annotations
 
-import re
-
 import numpy as np
 import pytest
 
@@ -13,15 +11,16 @@ from hierarchical_sparse_kv_resolve_amd.runner import layer_groups
 
 
 def test_recorded_traffic_matches_workload_schedule_and_source():
-    text = open(bench.TRAFFIC_PROFILE).read()
-    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
-    wl, sched = fields["workload"], fields["schedule"]
-    if fields["source_sha256"] == bench.gather_source_hash():
-        assert bench.recorded_traffic(wl, sched) == int(fields["traffic_bytes_per_launch"])
-    else:  # the gather source changed since the counters were taken
-        assert bench.recorded_traffic(wl, sched) is None
-    assert bench.recorded_traffic(wl, "prefetch:2") is None
-    assert bench.recorded_traffic("c4_speculative_verify", sched) is None
+    records = bench.traffic_records()
+    assert records, "no counter summaries under profiles/"
+    for fields in records:
+        wl, sched = fields["workload"], fields["schedule"]
+        if fields["source_sha256"] == bench.gather_source_hash():
+            assert bench.recorded_traffic(wl, sched) == int(fields["traffic_bytes_per_launch"])
+        else:  # the gather source changed since the counters were taken
+            assert bench.recorded_traffic(wl, sched) is None
+    assert bench.recorded_traffic("c2_glm_shared_indices", "no_such_schedule") is None
+    assert bench.recorded_traffic("no_such_workload", "fused") is None
 
 
 def test_launch_means_group_by_kernel():
