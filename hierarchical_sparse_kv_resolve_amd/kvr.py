@@ -4,7 +4,10 @@ Argument marshalling only: every entry point forwards raw device pointers,
 sizes and a HIP stream to the C ABI, and raises KvrError on a non-OK return.
 All work on the path runs in the library's HIP kernels; there is no fallback.
 Tensors may be torch tensors (their data_ptr() is passed), plain integer
-addresses, or None for NULL.  The stream defaults to torch's current stream.
+addresses, or None for NULL.  A torch tensor is checked against what the
+header says of its argument (on the GPU or pinned host memory, contiguous, at
+least the bytes the call reads or writes) before the call; addresses are
+passed as given.  The stream defaults to torch's current stream.
 """
 from __future__ import annotations
 
@@ -135,6 +138,42 @@ def _ptr(x) -> int | None:
     raise TypeError(f"cannot take the address of {type(x)}")
 
 
+def _dev(x, name: str, nbytes: int = 0) -> int | None:
+    """Address of a device argument.  A torch tensor must live on the GPU, be
+    contiguous and hold at least `nbytes` (the size the header's layout gives
+    it for this call), so that a host tensor or a short buffer raises here
+    instead of reaching a kernel.  Integer addresses and None pass unchecked."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "is_cuda"):
+        if not x.is_cuda:
+            raise TypeError(f"{name}: expected a GPU tensor, got one on {x.device}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name}: the tensor is not contiguous")
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name}: {have} bytes, the call needs {nbytes}")
+        return x.data_ptr()
+    raise TypeError(f"{name}: expected a GPU tensor or an address, got {type(x)}")
+
+
+def _pinned(x, name: str, nbytes: int = 0) -> int | None:
+    """Address of a pinned host argument (a torch tensor in pinned CPU memory,
+    or an address from host_alloc)."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "is_cuda"):
+        if x.is_cuda or not x.is_pinned():
+            raise TypeError(f"{name}: expected a pinned host tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"{name}: the tensor is not contiguous")
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name}: {have} bytes, the call needs {nbytes}")
+        return x.data_ptr()
+    raise TypeError(f"{name}: expected a pinned host tensor or an address, got {type(x)}")
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         import torch
@@ -198,72 +237,111 @@ class Context:
         except Exception:
             pass
 
+    def _sizes(self):
+        c = self.cfg
+        return (c.n_req, c.n_layers, c.history_rows, c.max_new_rows, c.page_rows, c.tail_rows,
+                c.hot_slots, c.row_bytes, c.pool_pages)
+
     def bind_metadata(self, L, page_map, host_valid, tag, stamp, clock):
-        _check(lib().kvr_bind_metadata(self.handle, _ptr(L), _ptr(page_map), _ptr(host_valid),
-                                       _ptr(tag), _ptr(stamp), _ptr(clock)))
+        N, _, H, _, P, _, B, _, _ = self._sizes()
+        npg = (H + P - 1) // P if P > 0 else 0
+        _check(lib().kvr_bind_metadata(self.handle, _dev(L, "L", 4 * N),
+                                       _dev(page_map, "page_map", 4 * N * npg),
+                                       _dev(host_valid, "host_valid", N * npg),
+                                       _dev(tag, "tag", 4 * N * B), _dev(stamp, "stamp", 4 * N * B),
+                                       _dev(clock, "clock", 4 * N)))
 
     def bind_layer(self, layer, tail, pool, hot, host):
-        _check(lib().kvr_bind_layer(self.handle, layer, _ptr(tail), _ptr(pool), _ptr(hot),
-                                    _ptr(host)))
+        N, _, H, M, P, T, B, R, pool_pages = self._sizes()
+        _check(lib().kvr_bind_layer(self.handle, layer, _dev(tail, "tail", N * T * R),
+                                    _dev(pool, "pool", pool_pages * P * R),
+                                    _dev(hot, "hot", N * B * R),
+                                    _pinned(host, "host", N * (H + M) * R)))
 
     def init_state(self, stream=None):
         _check(lib().kvr_init_state(self.handle, _stream(stream)))
 
     def append_rows(self, n, req_ids, new_rows, status=None, stream=None):
-        _check(lib().kvr_append_rows(self.handle, n, _ptr(req_ids), _ptr(new_rows), _ptr(status),
-                                     _stream(stream)))
+        _, NL, _, _, _, _, _, R, _ = self._sizes()
+        _check(lib().kvr_append_rows(self.handle, n, _dev(req_ids, "req_ids", 4 * n),
+                                     _dev(new_rows, "new_rows", NL * n * R),
+                                     _dev(status, "status", 4 * n), _stream(stream)))
+
+    def _resolve_args(self, n, req_ids, sel, sel_count, stride, loc, fills, fill_count, status,
+                      stats):
+        B = self.cfg.hot_slots
+        m = max(n, 0) * max(stride, 0)
+        return (_dev(req_ids, "req_ids", 4 * n), _dev(sel, "sel", 4 * m),
+                _dev(sel_count, "sel_count", 4 * n), _dev(loc, "loc", 4 * m),
+                _dev(fills, "fills", 8 * n * B), _dev(fill_count, "fill_count", 4 * n),
+                _dev(status, "status", 4 * n), _dev(stats, "stats", 8 * len(STATS_FIELDS)))
 
     def resolve_rows(self, n, req_ids, sel, sel_count, stride, loc, fills, fill_count, fill_layer,
                      status, stats=None, stream=None):
-        _check(lib().kvr_resolve_rows(self.handle, n, _ptr(req_ids), _ptr(sel), _ptr(sel_count),
-                                      stride, _ptr(loc), _ptr(fills), _ptr(fill_count), fill_layer,
-                                      _ptr(status), _ptr(stats), _stream(stream)))
+        rid, sl, sc, lc, fl, fc, st, sts = self._resolve_args(n, req_ids, sel, sel_count, stride,
+                                                              loc, fills, fill_count, status,
+                                                              stats)
+        _check(lib().kvr_resolve_rows(self.handle, n, rid, sl, sc, stride, lc, fl, fc, fill_layer,
+                                      st, sts, _stream(stream)))
 
     def append_resolve_rows(self, n, req_ids, new_rows, append_status, sel, sel_count, stride, loc,
                             fills, fill_count, fill_layer, status, stats=None, stream=None):
-        _check(lib().kvr_append_resolve_rows(self.handle, n, _ptr(req_ids), _ptr(new_rows),
-                                             _ptr(append_status), _ptr(sel), _ptr(sel_count),
-                                             stride, _ptr(loc), _ptr(fills), _ptr(fill_count),
-                                             fill_layer, _ptr(status), _ptr(stats),
+        NL, R = self.cfg.n_layers, self.cfg.row_bytes
+        rid, sl, sc, lc, fl, fc, st, sts = self._resolve_args(n, req_ids, sel, sel_count, stride,
+                                                              loc, fills, fill_count, status,
+                                                              stats)
+        _check(lib().kvr_append_resolve_rows(self.handle, n, rid,
+                                             _dev(new_rows, "new_rows", NL * n * R),
+                                             _dev(append_status, "append_status", 4 * n), sl, sc,
+                                             stride, lc, fl, fc, fill_layer, st, sts,
                                              _stream(stream)))
 
-    def gather_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None, stream=None):
+    def _gather_args(self, layers, n, req_ids, loc, count, stride, outs, status):
         nl = len(layers)
+        m = max(n, 0) * max(stride, 0)
+        R = self.cfg.row_bytes
+        if len(outs) != nl:
+            raise ValueError(f"outs: {len(outs)} buffers for {nl} layers")
         arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
-        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
-        _check(lib().kvr_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
-                                     _ptr(count), stride, arr_o, _ptr(status), _stream(stream)))
+        arr_o = (ctypes.c_void_p * max(1, nl))(*[_dev(o, "out", m * R) for o in outs])
+        return (nl, arr_l, _dev(req_ids, "req_ids", 4 * n), _dev(loc, "loc", 4 * m),
+                _dev(count, "count", 4 * n), arr_o, _dev(status, "status", 4 * n))
+
+    def gather_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None, stream=None):
+        nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(layers, n, req_ids, loc, count,
+                                                               stride, outs, status)
+        _check(lib().kvr_gather_rows(self.handle, nl, arr_l, n, rid, lc, cnt, stride, arr_o, st,
+                                     _stream(stream)))
 
     def gather_resident_rows(self, layers, n, req_ids, loc, count, stride, outs, status=None,
                              stream=None):
-        nl = len(layers)
-        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
-        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
-        _check(lib().kvr_gather_resident_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
-                                              _ptr(count), stride, arr_o, _ptr(status),
-                                              _stream(stream)))
+        nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(layers, n, req_ids, loc, count,
+                                                               stride, outs, status)
+        _check(lib().kvr_gather_resident_rows(self.handle, nl, arr_l, n, rid, lc, cnt, stride,
+                                              arr_o, st, _stream(stream)))
 
     def fill_gather_rows(self, layers, n, req_ids, loc, sel, count, stride, outs, status=None,
                          stream=None):
-        nl = len(layers)
-        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
-        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
-        _check(lib().kvr_fill_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
-                                          _ptr(sel), _ptr(count), stride, arr_o, _ptr(status),
-                                          _stream(stream)))
+        nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(layers, n, req_ids, loc, count,
+                                                               stride, outs, status)
+        sl = _dev(sel, "sel", 4 * max(n, 0) * max(stride, 0))
+        _check(lib().kvr_fill_gather_rows(self.handle, nl, arr_l, n, rid, lc, sl, cnt, stride,
+                                          arr_o, st, _stream(stream)))
 
     def fused_gather_rows(self, layers, n, req_ids, loc, sel, count, stride, outs, status=None,
                           stream=None):
-        nl = len(layers)
-        arr_l = (ctypes.c_int32 * max(1, nl))(*layers)
-        arr_o = (ctypes.c_void_p * max(1, nl))(*[_ptr(o) for o in outs])
-        _check(lib().kvr_fused_gather_rows(self.handle, nl, arr_l, n, _ptr(req_ids), _ptr(loc),
-                                           _ptr(sel), _ptr(count), stride, arr_o, _ptr(status),
-                                           _stream(stream)))
+        nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(layers, n, req_ids, loc, count,
+                                                               stride, outs, status)
+        sl = _dev(sel, "sel", 4 * max(n, 0) * max(stride, 0))
+        _check(lib().kvr_fused_gather_rows(self.handle, nl, arr_l, n, rid, lc, sl, cnt, stride,
+                                           arr_o, st, _stream(stream)))
 
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
-        _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _ptr(sel), _ptr(union_rows),
-                                                 _ptr(union_count), _ptr(map_), _stream(stream)))
+        m = max(n, 0) * max(q, 0) * max(k, 0)
+        _check(lib().kvr_dedup_verify_selections(self.handle, n, q, k, _dev(sel, "sel", 4 * m),
+                                                 _dev(union_rows, "union_rows", 4 * m),
+                                                 _dev(union_count, "union_count", 4 * n),
+                                                 _dev(map_, "map", 4 * m), _stream(stream)))
 
     def timing_begin(self, capacity: int):
         """Record the duration of each kernel this context launches from now on
@@ -285,21 +363,30 @@ class Context:
         return [(KERNEL_NAMES[k], float(t)) for k, t in zip(kinds[:m], ms[:m])]
 
     def reclaim_pages(self, n, req_ids, pages, freed_phys, status=None, stream=None):
-        _check(lib().kvr_reclaim_pages(self.handle, n, _ptr(req_ids), _ptr(pages),
-                                       _ptr(freed_phys), _ptr(status), _stream(stream)))
+        _check(lib().kvr_reclaim_pages(self.handle, n, _dev(req_ids, "req_ids", 4 * n),
+                                       _dev(pages, "pages", 4 * n),
+                                       _dev(freed_phys, "freed_phys", 4 * n),
+                                       _dev(status, "status", 4 * n), _stream(stream)))
 
     def restore_pages(self, n, req_ids, pages, phys, status=None, stream=None):
-        _check(lib().kvr_restore_pages(self.handle, n, _ptr(req_ids), _ptr(pages), _ptr(phys),
-                                       _ptr(status), _stream(stream)))
+        _check(lib().kvr_restore_pages(self.handle, n, _dev(req_ids, "req_ids", 4 * n),
+                                       _dev(pages, "pages", 4 * n), _dev(phys, "phys", 4 * n),
+                                       _dev(status, "status", 4 * n), _stream(stream)))
 
     def reuse_locations(self, mode, dst_layers, n, req_ids, src_loc, dst_loc, count, stride,
                         fills=None, fill_count=None, status=None, stream=None):
         layers = list(dst_layers or [])
         arr_l = (ctypes.c_int32 * max(1, len(layers)))(*layers)
-        _check(lib().kvr_reuse_locations(self.handle, mode, len(layers), arr_l, n, _ptr(req_ids),
-                                         _ptr(src_loc), _ptr(dst_loc), _ptr(count), stride,
-                                         _ptr(fills), _ptr(fill_count), _ptr(status),
-                                         _stream(stream)))
+        m = max(n, 0) * max(stride, 0)
+        B = self.cfg.hot_slots
+        _check(lib().kvr_reuse_locations(self.handle, mode, len(layers), arr_l, n,
+                                         _dev(req_ids, "req_ids", 4 * n),
+                                         _dev(src_loc, "src_loc", 4 * m),
+                                         _dev(dst_loc, "dst_loc", 4 * m),
+                                         _dev(count, "count", 4 * n),
+                                         stride, _dev(fills, "fills", 8 * n * B),
+                                         _dev(fill_count, "fill_count", 4 * n),
+                                         _dev(status, "status", 4 * n), _stream(stream)))
 
 
 class Residency:
@@ -376,8 +463,12 @@ class DraftRing:
 
     def __init__(self, n_req, window, capacity, row_bytes, ring, length, high):
         h = ctypes.c_void_p()
-        _check(lib().kvr_draft_create(n_req, window, capacity, row_bytes, _ptr(ring), _ptr(length),
-                                      _ptr(high), ctypes.byref(h)))
+        self.n_req, self.window_rows, self.row_bytes = n_req, window, row_bytes
+        _check(lib().kvr_draft_create(n_req, window, capacity, row_bytes,
+                                      _dev(ring, "ring", max(n_req, 0) * max(capacity, 0) *
+                                           max(row_bytes, 0)),
+                                      _dev(length, "length", 4 * max(n_req, 0)),
+                                      _dev(high, "high", 4 * max(n_req, 0)), ctypes.byref(h)))
         self.handle = h.value
 
     def close(self):
@@ -395,16 +486,21 @@ class DraftRing:
         _check(lib().kvr_draft_reset(self.handle, _stream(stream)))
 
     def append(self, n, req_ids, rows_each, rows, status=None, stream=None):
-        _check(lib().kvr_draft_append(self.handle, n, _ptr(req_ids), rows_each, _ptr(rows),
-                                      _ptr(status), _stream(stream)))
+        need = max(n, 0) * max(rows_each, 0) * self.row_bytes
+        _check(lib().kvr_draft_append(self.handle, n, _dev(req_ids, "req_ids", 4 * n), rows_each,
+                                      _dev(rows, "rows", need), _dev(status, "status", 4 * n),
+                                      _stream(stream)))
 
     def rollback(self, n, req_ids, keep, status=None, stream=None):
-        _check(lib().kvr_draft_rollback(self.handle, n, _ptr(req_ids), _ptr(keep), _ptr(status),
+        _check(lib().kvr_draft_rollback(self.handle, n, _dev(req_ids, "req_ids", 4 * n),
+                                        _dev(keep, "keep", 4 * n), _dev(status, "status", 4 * n),
                                         _stream(stream)))
 
     def window(self, n, req_ids, out, visible=None, status=None, stream=None):
-        _check(lib().kvr_draft_window(self.handle, n, _ptr(req_ids), _ptr(out), _ptr(visible),
-                                      _ptr(status), _stream(stream)))
+        need = max(n, 0) * self.window_rows * self.row_bytes
+        _check(lib().kvr_draft_window(self.handle, n, _dev(req_ids, "req_ids", 4 * n),
+                                      _dev(out, "out", need), _dev(visible, "visible", 4 * n),
+                                      _dev(status, "status", 4 * n), _stream(stream)))
 
 
 class StagingPool:

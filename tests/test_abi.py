@@ -96,3 +96,19 @@ def test_speculative_state_rejects_bad_shapes():
     assert lib.kvr_staging_create(0, ctypes.byref(out)) == kvr.E_ARG
     assert lib.kvr_staging_acquire(None, None, None) == kvr.E_ARG
     assert lib.kvr_staging_release(None, 0, None) == kvr.E_ARG
+
+
+def test_binding_argument_checks_on_the_host():
+    """The binding's own checks that need no GPU: host tensors and arrays are
+    refused as device arguments, unpinned tensors as the host store, and plain
+    addresses and NULL pass through unchanged."""
+    import torch
+    with pytest.raises(TypeError, match="expected a GPU tensor"):
+        kvr._dev(torch.zeros(4), "sel")
+    with pytest.raises(TypeError, match="or an address"):
+        kvr._dev(np.zeros(4), "sel")
+    with pytest.raises(TypeError, match="pinned host tensor"):
+        kvr._pinned(torch.zeros(4), "host")
+    assert kvr._dev(None, "status") is None
+    assert kvr._dev(4096, "sel", 1 << 40) == 4096
+    assert kvr._pinned(8192, "host", 1 << 40) == 8192

@@ -411,9 +411,55 @@ def test_fused_entry_points_reject_missing_arguments():
             gpu.ctx.append_resolve_rows(n, None, None, None, sel, None, k, loc, fills, fc, -1, st)
         assert e.value.code == kvr.E_ARG and "new_rows" in str(e.value)
         with pytest.raises(kvr.KvrError) as e:
-            gpu.ctx.append_resolve_rows(n, None, sel, None, sel, None, cfg.sel_cap + 1, loc,
-                                        fills, fc, -1, st)
+            # addresses, not tensors: the binding passes them on unchecked, so
+            # the library's own stride check answers
+            gpu.ctx.append_resolve_rows(n, None, sel.data_ptr(), None, sel.data_ptr(), None,
+                                        cfg.sel_cap + 1, loc.data_ptr(), fills, fc, -1, st)
         assert e.value.code == kvr.E_ARG and "stride" in str(e.value)
+        torch.cuda.synchronize()
+        st0 = gpu.state()
+        assert (st0["L"] == cfg.H).all()  # nothing ran
+    finally:
+        gpu.close()
+
+
+def test_binding_rejects_host_short_and_strided_tensors():
+    """The binding checks torch tensors against the header's layout before a
+    call: a host tensor, a buffer shorter than the call reads or writes, or a
+    non-contiguous view raises and nothing is launched."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2)
+    inputs = Inputs(cfg)
+    gpu = _gpu_run(inputs)
+    try:
+        n, k = cfg.n_req, cfg.k
+        assert n > 1 and k > 1  # so that the views below are short or strided
+        dev = "cuda"
+        sel = torch.zeros((n, k), dtype=torch.int32, device=dev)
+        loc = torch.zeros((n, k), dtype=torch.int32, device=dev)
+        fills = torch.zeros((n, cfg.B, 2), dtype=torch.int32, device=dev)
+        fc = torch.zeros(n, dtype=torch.int32, device=dev)
+        st = torch.zeros(n, dtype=torch.int32, device=dev)
+        outs = [torch.zeros((n, k, cfg.R), dtype=torch.uint8, device=dev)]
+        with pytest.raises(TypeError, match="sel: expected a GPU tensor"):
+            gpu.ctx.resolve_rows(n, None, sel.cpu(), None, k, loc, fills, fc, -1, st)
+        short_fills = torch.zeros((n, cfg.B // 2, 2), dtype=torch.int32, device=dev)
+        with pytest.raises(ValueError, match="fills: .* the call needs"):
+            gpu.ctx.resolve_rows(n, None, sel, None, k, loc, short_fills, fc, -1, st)
+        with pytest.raises(ValueError, match="loc: .* the call needs"):
+            gpu.ctx.resolve_rows(n, None, sel, None, k, loc[:1], fills, fc, -1, st)
+        with pytest.raises(ValueError, match="not contiguous"):
+            gpu.ctx.gather_rows([0], n, None, loc.t(), None, k, outs)
+        short_out = torch.zeros((n, k // 2, cfg.R), dtype=torch.uint8, device=dev)
+        with pytest.raises(ValueError, match="out: .* the call needs"):
+            gpu.ctx.gather_rows([0], n, None, loc, None, k, [short_out])
+        with pytest.raises(ValueError, match="2 buffers for 1 layers"):
+            gpu.ctx.fused_gather_rows([0], n, None, loc, sel, None, k, outs * 2)
+        with pytest.raises(TypeError, match="host: expected a pinned host tensor"):
+            gpu.ctx.bind_layer(0, gpu.tail[0] if cfg.T else None,
+                               gpu.pool[0] if cfg.pool_pages else None, gpu.hot[0],
+                               torch.zeros(8, dtype=torch.uint8))
         torch.cuda.synchronize()
         st0 = gpu.state()
         assert (st0["L"] == cfg.H).all()  # nothing ran
