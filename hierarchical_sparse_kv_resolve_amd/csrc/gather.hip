@@ -137,6 +137,13 @@ __global__ __launch_bounds__(NT) void gather_kernel(GatherArgs a)
 // per layer drawing on the host link.
 constexpr int kFillTile = 1024;
 constexpr int kFillPer = kFillTile / NT;  // entries per thread of a full job
+// 16-byte host loads in flight per lane in the copy loop: twice the refill's,
+// so a worker keeps 64 KiB of host reads in flight and the last workers of a
+// launch drain it faster (measured best of 8, 12, 16, 20 and 24 for the GLM
+// shape; 20 and 24 are marginally better only at the verify and long-context
+// shapes).  It costs occupancy (3 waves per SIMD), which the resident tiles of
+// the fused launch do not miss.
+constexpr int kFillUnroll = 16;
 constexpr int kFillTileMin = 16;
 constexpr int kFillJobsMin = 16;
 
@@ -203,18 +210,18 @@ __device__ __forceinline__ void fill_jobs(const GatherArgs &a, int t, int worker
         uint8_t *hot = lp.hot + (int64_t)r * a.sh.B * R;
         uint8_t *out = a.out[t] + (int64_t)i * a.stride * R;
         const int total = fl.n * C;
-        for (int c0 = 0; c0 < total; c0 += NT * kUnroll) {
-            u32x4 v[kUnroll];
-            int rr[kUnroll];
+        for (int c0 = 0; c0 < total; c0 += NT * kFillUnroll) {
+            u32x4 v[kFillUnroll];
+            int rr[kFillUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kFillUnroll; ++u) {
                 const int c = c0 + u * NT + threadIdx.x;
                 rr[u] = c < total ? c / C : -1;
                 if (rr[u] >= 0)
                     load_chunk(v[u], src + (int64_t)fl.row[rr[u]] * R + (c - rr[u] * C) * 16);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kFillUnroll; ++u) {
                 if (rr[u] < 0)
                     continue;
                 const int off = (c0 + u * NT + (int)threadIdx.x - rr[u] * C) * 16;
