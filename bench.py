@@ -105,6 +105,19 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def auto_fused(cfg) -> bool:
+    """The default schedule: fused where several payload layers share the
+    indices (their resident gathers are big enough to hide under the fill
+    pass) or one physical source serves several resolving layers (each
+    layer's gather leaves the chain of fills); with one payload layer and one
+    resolve the refill in ascending row order reads the host faster, unless
+    the call is so small that latency rules (a launch fewer then counts most).
+    """
+    return ((cfg.reuse == "distinct" and cfg.payload_layers > 1)
+            or (cfg.reuse != "distinct" and cfg.groups > 1)
+            or cfg.n_req * cfg.sel_cap <= 4096)
+
+
 def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None):
     """The oracle as it stands, on this host's cores (or `threads` of them),
     over the same decode steps from a fresh state; the pass is repeated (state
@@ -427,17 +440,7 @@ def main():
     counts = rows_per_group(inputs, range(W, total))
     pg = args.prefetch_groups
     pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
-    # auto: fused where several payload layers share the indices (their
-    # resident gathers are big enough to hide under the fill pass) or one
-    # physical source serves several resolving layers (each layer's gather
-    # leaves the chain of fills); with one payload layer and one resolve the
-    # refill in ascending row order reads the host faster, unless the call
-    # is so small that latency rules (a launch fewer then counts most)
-    fused = args.schedule == "fused" or (
-        args.schedule == "auto"
-        and ((cfg.reuse == "distinct" and cfg.payload_layers > 1)
-             or (cfg.reuse != "distinct" and cfg.groups > 1)
-             or cfg.n_req * cfg.sel_cap <= 4096))
+    fused = args.schedule == "fused" or (args.schedule == "auto" and auto_fused(cfg))
     no_graph = args.no_graph
     if fused and cfg.reuse != "distinct" and not no_graph:
         # its graph capture is disabled (GpuRun.capture): timed eagerly

@@ -783,6 +783,51 @@ def test_graph_replays_match_oracle(shape, prefetch_groups, fused):
         gpu.close()
 
 
+@pytest.mark.parametrize("c", [1, 2, 3, 4])
+def test_bench_configuration_parity(c):
+    """The configuration bench.py times, at full size: its default schedule,
+    4 eager warm-up steps, then the 28 timed steps captured into one HIP graph
+    and replayed twice from the same snapshot.  After each replay the last
+    step's locations, fills and gathered bytes, the metadata and the hot
+    payload equal the oracle's after all 32 steps."""
+    import torch
+    import bench
+    cfg = FULL[c].with_(steps=32)
+    fused = bench.auto_fused(cfg)
+    assert not (fused and cfg.reuse != "distinct")  # captured, as bench.py does
+    warm, pg = 4, 2
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    print(f"[bench-config] {cfg.name}: fused={fused}", flush=True)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    try:
+        gpu.stage(range(cfg.steps))
+        for s in range(warm):
+            gpu.step(s, prefetch_groups=pg, fused=fused)
+        torch.cuda.synchronize()
+        snap = gpu.snapshot()
+        graph = gpu.capture(range(warm, cfg.steps), prefetch_groups=pg, fused=fused)
+        torch.cuda.synchronize()
+        for s in range(cfg.steps):
+            o = run.step(s)
+        for rep in range(2):
+            if rep:
+                gpu.restore(snap)
+            graph.replay()
+            torch.cuda.synchronize()
+            for g in range(cfg.groups):
+                _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
+            _compare_state(gpu, run, reqs)
+            assert (gpu.gather_status.cpu().numpy() == 0).all()
+            assert (gpu.append_status.cpu().numpy() == 0).all()
+            for l in range(cfg.payload_layers):
+                assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l]), f"hot {l}"
+        print(f"[bench-config] {cfg.name}: ok", flush=True)
+    finally:
+        gpu.close()
+
+
 @pytest.mark.gpu
 def test_launch_timing_records_each_kernel():
     """Launch timing records every kernel of a step in launch order with a
