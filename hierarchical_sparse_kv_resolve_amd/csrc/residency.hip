@@ -280,7 +280,7 @@ int kvr_residency_admit(kvr_residency *res, int64_t need, int32_t n_order, const
         deficit -= cnt;
     }
     if (deficit > 0)
-        return kvr::api_fail(KVR_E_CAPACITY, "optional pages cannot cover the deficit");
+        return kvr::api_fail(KVR_E_CAPACITY, "the shortfall is larger than all optional pages");
     if (planned > cap)
         return kvr::api_fail(KVR_E_ARG, "the reclaim list needs %lld entries, cap is %d",
                              (long long)planned, cap);

@@ -3,8 +3,8 @@
 // Follows "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
 // Hierarchy", section "How it works", paragraph "Resolution": a selected row
 // is taken from the tail or a ready optional-history page if it is there,
-// else from the B-slot hot cache (with LRU stamps), else it is copied from
-// pinned host memory into an LRU victim slot.  The host copy itself is done
+// else from the B-slot hot cache (with LRU stamps), else its host-store copy
+// is brought into an LRU victim slot.  The host copy itself is done
 // by the refill or fill kernels (copy.hip, gather.hip) from the fill list or
 // the location words written here.  On request the same launch first appends
 // each request's decoded row (the tail write of "Memory split").

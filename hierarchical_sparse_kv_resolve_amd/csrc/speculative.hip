@@ -1,7 +1,8 @@
 // Speculative state ("Adaptive DHiSparse: Speculative Decoding over a
 // Load-Adaptive KV Hierarchy", section "How it works", paragraph "Speculative
-// state"): the drafter keeps only its visible window, in a ring buffer, and
-// target layers reuse verification staging once their consumers complete.
+// state"): the drafter stores just the rows it can still see, in a ring, and
+// the target layers hand a verification staging buffer out again only after
+// the kernels that read it have finished.
 //
 // Drafter ring: per request a ring of C rows (slot = position mod C) of which
 // the last W positions are visible; C - W extra slots let drafted rows that

@@ -418,7 +418,7 @@ class Residency:
 
     def admit(self, need: int, order):
         """(True, [(request, page), ...] to reclaim, handle), or (False, [], -1)
-        when the optional pages cannot cover the deficit."""
+        when the shortfall is larger than all optional pages together."""
         import numpy as np
         order = np.ascontiguousarray(order, dtype=np.int32)
         cap = self.n_req * self.n_complete

@@ -3,14 +3,17 @@
  *
  * The method is the resolver of "Adaptive DHiSparse: Speculative Decoding over
  * a Load-Adaptive KV Hierarchy" (section "How it works"):
- *   - Memory split: every (request, KV source) owns a fixed hot cache of B
- *     rows, a mutable tail and metadata; complete pages of imported history can
- *     also sit, ready, in an optional pool shared by all requests.
- *   - Resolution: each selected row is looked up, in order and stopping at the
- *     first hit, in (1) the tail and the ready optional-history page map,
- *     (2) the hot cache, scanning at most B slots, with LRU replacement,
- *     (3) pinned host memory, copied into the hot cache.
- *   - Speculative state: verification queries share missing-row retrieval.
+ *   - Memory split: each request has, per KV source, its own B-slot hot
+ *     cache, a writable tail and its metadata; whole pages of the history it
+ *     was admitted with may in addition be kept ready in an optional pool that
+ *     all requests share.
+ *   - Resolution: a selected row is taken from the first of three places that
+ *     holds it: (1) the tail, else a ready page found through the optional
+ *     page map; (2) the hot cache, whose lookup examines no more than B slots
+ *     and which is managed LRU; (3) the pinned host store, from which the row
+ *     is copied into a hot-cache slot.
+ *   - Speculative state: the queries of one verification block fetch each
+ *     missing row once between them.
  *   - Model-specific reuse: Reuse layers inherit a location vector when they
  *     share one physical KV source; layers that share sparse indices but own
  *     distinct payloads fetch the same positions for their own payload.
@@ -276,9 +279,9 @@ int kvr_reuse_locations(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
                         void *stream);
 
 /* Optional-pool residency ("Adaptive DHiSparse", section "How it works",
- * paragraph "Reclamation and refill"): every row stays either ready on the
- * GPU or backed up in host memory, pages are released only after their host
- * backup and after earlier readers, and released pages are refilled later.
+ * paragraph "Reclamation and refill"): no row is ever lost, since a page
+ * leaves the GPU only with a host backup in place and only once the kernels
+ * that read it earlier are done; pages taken away are brought back later.
  *
  * kvr_reclaim_pages: the listed (req_ids[i], pages[i]) optional pages stop
  * being ready.  A page without a host copy first gets one (its P rows of
@@ -318,13 +321,14 @@ int kvr_restore_pages(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const int
  *   map, of which the first n_complete pages per request may be optional;
  *   pool_pages physical pages in the pool, those no page maps are free.
  * kvr_residency_admit: an admission needing `need` physical pages.  Free
- *   pages are used first; for the rest (the deficit) whole requests' ready
- *   pages are taken, walking `order` (n_order request ids, the reclaim
- *   order), until the deficit is covered; the other requests keep theirs.
- *   The lowest free page ids are reserved for the admission.  Writes the
- *   (request, page) list to reclaim, in that order (at most `cap` entries),
- *   and a handle.  Returns KVR_E_CAPACITY when the optional pages cannot
- *   cover the deficit (the admission waits; nothing changes, *n_out = 0),
+ *   pages are used first; the pages still missing (the shortfall) come from
+ *   requests that give up every ready page they hold, one request at a time
+ *   in `order` (n_order request ids, the reclaim order), until enough are
+ *   free; the requests after that keep theirs.  The lowest free page ids are
+ *   reserved for the admission.  Writes the (request, page) list to reclaim,
+ *   in that order (at most `cap` entries), and a handle.  Returns
+ *   KVR_E_CAPACITY when the shortfall is larger than all optional pages
+ *   together (the admission waits; nothing changes, *n_out = 0),
  *   KVR_E_ARG when the list would exceed `cap` (nothing changes).
  * kvr_residency_release: the admission drained; its pages are free again.
  * kvr_residency_refill: bounded round-robin refill of the pages that
@@ -354,7 +358,8 @@ int kvr_residency_counts(const kvr_residency *res, int64_t *free_pages, int64_t 
 /* Speculative state ("Adaptive DHiSparse", section "How it works",
  * paragraph "Speculative state").
  *
- * Drafter visible-window ring: the drafter keeps only its visible window.  Per
+ * Drafter visible-window ring: the drafter stores no more than the rows it can
+ * still see.  Per
  * request, drafter rows are numbered by position; row p lives in slot p mod C
  * of a ring of C >= W slots; the visible window is the last min(W, length)
  * positions.  The C - W extra slots let rows that verification rejects be

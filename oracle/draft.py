@@ -5,7 +5,7 @@ It shares no code with the GPU library.
 
 Follows "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
 Hierarchy", section "How it works", paragraph "Speculative state": the
-drafter keeps only its visible window, in a ring buffer.
+drafter stores just the rows it can still see, in a ring.
 
 Readings where the page is silent:
   * a request's drafter rows are numbered by position 0, 1, 2, ...; `length`

@@ -8,16 +8,18 @@
  * Decoding over a Load-Adaptive KV Hierarchy" (page 1 of the source pages).
  *
  * What the page fixes (section "How it works"):
- *   - Memory split: each (request, KV source) owns a fixed hot cache of B
- *     rows, a mutable tail and metadata; complete pages of imported history
- *     may additionally sit in an optional, reclaimable pool.
- *   - Reclamation and refill: every row is either ready on the GPU or has a
- *     host copy.
- *   - Resolution: for each selected row check, in order, (1) the tail and the
- *     ready optional-history map, (2) the hot cache, scanning at most B slots,
- *     with LRU replacement, (3) a copy from pinned host memory into the hot
- *     cache; stop at the first place that has the row.
- *   - Speculative state: verification queries share missing-row retrieval.
+ *   - Memory split: per KV source, a request has its own B-slot hot cache,
+ *     a writable tail and its metadata; whole pages of the history it arrived
+ *     with may also be kept in an optional pool that can be taken back.
+ *   - Reclamation and refill: no row is ever only in a released page: it is
+ *     ready on the GPU, in host memory, or both.
+ *   - Resolution: for each selected row try, in this order, (1) the tail,
+ *     then the ready pages through the optional map, (2) the hot cache, where
+ *     a lookup examines at most B slots and replacement is LRU, (3) the
+ *     pinned host store, whose row is copied into a hot-cache slot; the first
+ *     place that has the row wins.
+ *   - Speculative state: the queries of one verification block fetch each
+ *     missing row once between them.
  *   - Model-specific reuse: Reuse layers inherit a location vector (one
  *     physical source); shared indices with distinct payloads replay the same
  *     positions per layer.

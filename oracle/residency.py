@@ -6,14 +6,16 @@ policy (a separate C++ implementation).
 
 Follows "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV
 Hierarchy", section "How it works":
-  * paragraph "Memory split": complete pages of imported history may sit in
-    reclaimable optional capacity next to the reserve admissions draw from
-    (required + optional + admission reserve within the pool);
-  * paragraph "Reclamation and refill": an admission that leaves a deficit
-    takes whole requests' optional pages, walking the requests in reclaim
-    order, until the deficit is covered; the other requests keep theirs; if
-    the optional pages cannot cover it the admission waits; refill is bounded
-    round-robin.
+  * paragraph "Memory split": whole pages of the history a request was
+    admitted with may be held as optional capacity that can be taken back,
+    beside the reserve that admissions use (the pool holds required,
+    optional and reserve pages);
+  * paragraph "Reclamation and refill": when an admission needs more pages
+    than are free, requests give up all their optional pages, one request at
+    a time in reclaim order, until the shortfall is met, and the requests
+    after that keep theirs; when even all optional pages would not be enough
+    the admission waits; refill brings pages back a bounded number at a
+    time, visiting requests in turn.
 
 Readings where the pages are silent:
   * the reclaim order is the caller's (a list of request ids);
@@ -57,7 +59,7 @@ class ResidencyPolicy:
     def admit(self, need: int, order):
         """An admission needing `need` physical pages.  Returns (True, the
         (request, page) list to reclaim, handle) or (False, [], -1) when the
-        optional pages cannot cover the deficit (nothing changes)."""
+        shortfall is larger than all optional pages together (nothing changes)."""
         assert need >= 0
         deficit = need - len(self.free)
         plan = []

@@ -1,7 +1,7 @@
 """Pins of the residency reference (oracle/residency.py and the page
 reclaim/restore of oracle/kvr_oracle.c) against facts fixed independently of
-it: the payload closed form, the invariant that every row is ready or has a
-host copy, a hand-worked admission and refill, and properties the pages'
+it: the payload closed form, the invariant that no row is ever without both
+a ready page and a host backup, a hand-worked admission and refill, and properties the pages'
 paragraph "Reclamation and refill" fixes (whole requests in reclaim order,
 the deficit covered and no more requests than needed, bounded round-robin).
 CPU only."""
