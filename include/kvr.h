@@ -394,8 +394,8 @@ int kvr_draft_rollback(kvr_draft *d, int32_t n, const int32_t *req_ids, const in
 int kvr_draft_window(kvr_draft *d, int32_t n, const int32_t *req_ids, void *out,
                      int32_t *visible, int32_t *status, void *stream);
 
-/* Verification staging reuse: target layers reuse staging buffers once their
- * consumers complete.  A pool of n_buffers caller-owned buffers, named by
+/* Verification staging reuse: a target layer's staging buffer is handed out
+ * again only after the kernels that read it have finished.  A pool of n_buffers caller-owned buffers, named by
  * index and handed out round-robin.  kvr_staging_acquire makes `stream` wait
  * until the buffer's previous consumer has released it; kvr_staging_release
  * records that release on the consumer's stream after its last read of the

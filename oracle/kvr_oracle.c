@@ -349,7 +349,7 @@ int orc_gather_one(const orc_source *s, int32_t layer, int32_t r, const uint32_t
 
 /* ---------------------------------------------------------------- dedup */
 
-/* The q selections of one verification block share missing-row retrieval:
+/* The q selections of one verification block fetch each missing row once:
  * their union (ascending, distinct) is resolved once, and map[qi][j] is the
  * union index of sel[qi][j].  sel, map: [q][k]; union_rows: [q * k]. */
 int orc_dedup_one(int32_t q, int32_t k, const int32_t *sel, int32_t *union_rows,
