@@ -219,6 +219,8 @@ template <int EK, int EB>
 __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
 {
     static_assert(EB <= kCntE && 2 * kCntE * NW == 4 * kWave, "compaction counter layout");
+    // the instances that spill unless the stamp-range reductions are pinned
+    constexpr bool kPinRange = EK >= 8 || (EK >= 4 && EB >= 8);
     extern __shared__ __align__(16) uint8_t lds[];
     uint64_t *sKey = reinterpret_cast<uint64_t *>(lds);
     int32_t *hkey = reinterpret_cast<int32_t *>(sKey + a.vc);
@@ -397,12 +399,20 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         return;
     }
     const uint32_t now = clk + 1;
+    // The block's stamp range.  The compiler loads the 2*NW per-wave values
+    // here and reduces them at the range's first use in step 3, which hides
+    // the reduction but keeps all of them live across step 2; in the largest
+    // instances that spills registers to scratch (reloaded on step 3's
+    // critical path, about 4 us), so there the empty asm makes the reduction
+    // happen here.
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         lo = sRedU[w] < lo ? sRedU[w] : lo;
         hi = sRedU[NW + w] > hi ? sRedU[NW + w] : hi;
     }
+    if constexpr (kPinRange)
+        asm volatile("" : "+v"(lo), "+v"(hi));
 
     // Step 2: every tag is looked up once among the pending rows.  If two
     // slots ever held one row, the lower slot is the hit.
@@ -662,12 +672,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
             }
         }
         __syncthreads();
-        uint32_t gl = 0xFFFFFFFFu, gh = 0;
+        uint32_t gl = 0xFFFFFFFFu, gh = 0;  // the same for the candidates older than tau
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             gl = sRedU[w] < gl ? sRedU[w] : gl;
             gh = sRedU[NW + w] > gh ? sRedU[NW + w] : gh;
         }
+        if constexpr (kPinRange)
+            asm volatile("" : "+v"(gl), "+v"(gh));
 #pragma unroll
         for (int e = 0; e < EB; ++e) {
             if ((blt[e] >> lane_id()) & 1) {
