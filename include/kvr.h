@@ -41,6 +41,14 @@
  *     complete normally.
  *   - Return codes are kvr_status values; kvr_last_error() gives a message for
  *     the calling thread's last failure.  No C++ exception leaves the library.
+ *   - Threads and streams: the calls that launch work only read the context,
+ *     so several host threads may issue them at once, except while launch
+ *     timing is on (kvr_timing_begin to kvr_timing_end records into the
+ *     context); kvr_bind_*, kvr_timing_* and kvr_destroy need the caller to
+ *     keep every other call on that context out meanwhile.  On the device,
+ *     calls that touch the same request must be ordered (one stream, or
+ *     events between streams): two resolves of one request in flight at once
+ *     race on its tags, stamps and clock.
  *
  * Location word (uint32): bits 31..30 give the place (kvr_place), bits 29..0
  * the index in it: the tail ring slot (pos mod T), the optional-pool row
