@@ -139,9 +139,41 @@ def _random_scenario(rng):
     return H, P, T, B, page_map, host_valid
 
 
+def _brute_stats(stats, bst, bloc, bfills, R):
+    """Add one resolve call's counters, derived from the brute model's
+    outcome, to `stats` (keyed like orc.STAT_NAMES): every call counts; a
+    failed call counts an error and nothing else; a good call counts its
+    entries by place (hot-cache entries split by the fresh flag into hits and
+    misses) and its fills, each of R host bytes (layer 0 is filled)."""
+    stats["calls"] += 1
+    if bst != 0:
+        stats["error"] += 1
+        return
+    for place, idx in bloc:
+        if place == 0:
+            stats["tail"] += 1
+        elif place == 1:
+            stats["page"] += 1
+        elif idx & FRESH:
+            stats["miss"] += 1
+        else:
+            stats["hit"] += 1
+    stats["fill"] += len(bfills)
+    stats["host_bytes"] += len(bfills) * R
+
+
+def _brute_residency_holds(bf, L):
+    """Every imported row below L is in the tail, in a ready page or has a
+    host copy (from the brute model's place sets)."""
+    tail, ready = bf.tail_rows(), bf.ready_rows()
+    return all(pos in tail or pos in ready or bf.host_valid[pos // bf.P]
+               for pos in range(min(L, bf.H)))
+
+
 @pytest.mark.parametrize("chunk", range(6))
 def test_oracle_equals_brute_force(chunk):
     counts = {}
+    broken = 0
     for seed in range(chunk * 300, chunk * 300 + 300):
         rng = np.random.default_rng(seed)
         H, P, T, B, page_map, host_valid = _random_scenario(rng)
@@ -149,6 +181,7 @@ def test_oracle_equals_brute_force(chunk):
         src = one_request_source(H, P, T, B, page_map, host_valid, R=16, n_layers=n_layers,
                                  max_new=12, seed=seed)
         bf = BruteSource(H, P, T, B, page_map, host_valid, n_layers=n_layers)
+        stats = dict.fromkeys(orc.STAT_NAMES, 0)
         for _ in range(int(rng.integers(1, 12))):
             if rng.random() < 0.5 and src.L[0] < H + 12:
                 assert src.append(new_row(src, int(src.L[0]), seed=seed))[0] == orc.OK
@@ -161,6 +194,8 @@ def test_oracle_equals_brute_force(chunk):
             loc, fills, fc, st = src.resolve(sel[None].astype(np.int32))
             bst, bloc, bfills = bf.resolve(sel.tolist())
             counts[bst] = counts.get(bst, 0) + 1
+            _brute_stats(stats, bst, bloc, bfills, 16)
+            assert dict(zip(orc.STAT_NAMES, src.stats.tolist())) == stats, seed
             assert st[0] == bst, (seed, sel)
             assert src.tag[0].tolist() == bf.tags(), seed
             assert src.stamp[0].tolist() == bf.stamps(), seed
@@ -180,8 +215,13 @@ def test_oracle_equals_brute_force(chunk):
                 assert labels == sel.tolist()
                 assert np.array_equal(out[0], payload_np(l, 0, np.array(labels, dtype=np.int64),
                                                          16, seed).reshape(k, 16))
-        assert src.check()[0] & ~1 == 0
+        # the residency bit is set exactly when the scenario broke the
+        # invariant for a row below L that is outside the tail
+        holds = _brute_residency_holds(bf, int(src.L[0]))
+        broken += not holds
+        assert src.check()[0] == (0 if holds else 1), seed
     assert counts.get(0, 0) > 500 and counts.get(orc.E_CAPACITY, 0) > 10
+    assert broken > 5
 
 
 @settings(max_examples=400, deadline=None, derandomize=True, database=None)
@@ -202,6 +242,7 @@ def test_oracle_equals_brute_force_hypothesis(B, T, P, H, data):
     src = one_request_source(H, P, T, B, page_map, host_valid, R=16, n_layers=1, max_new=20,
                              seed=5)
     bf = BruteSource(H, P, T, B, page_map, host_valid, n_layers=1)
+    stats = dict.fromkeys(orc.STAT_NAMES, 0)
     for _ in range(data.draw(st.integers(1, 20))):
         if data.draw(st.booleans()) and src.L[0] < H + 20:
             assert src.append(new_row(src, int(src.L[0]), seed=5))[0] == orc.OK
@@ -210,6 +251,8 @@ def test_oracle_equals_brute_force_hypothesis(B, T, P, H, data):
         sel = data.draw(st.lists(st.integers(0, L - 1), max_size=8))
         loc, fills, fc, st_ = src.resolve(np.array([sel], dtype=np.int32).reshape(1, len(sel)))
         bst, bloc, bfills = bf.resolve(sel)
+        _brute_stats(stats, bst, bloc, bfills, 16)
+        assert dict(zip(orc.STAT_NAMES, src.stats.tolist())) == stats
         assert st_[0] == bst
         assert src.tag[0].tolist() == bf.tags() and src.stamp[0].tolist() == bf.stamps()
         assert int(src.clock[0]) == bf.clock
@@ -217,6 +260,73 @@ def test_oracle_equals_brute_force_hypothesis(B, T, P, H, data):
         if bst == orc.OK:
             assert loc[0].tolist() == [word(p, i) for p, i in bloc]
         assert src.check()[0] == 0
+
+
+# ----------------------------------------------------------------- invariant check
+
+
+def test_check_reports_each_invariant_violation():
+    """The state check returns the exact bit of each invariant a hand-built
+    state breaks (1: a row below L that is in neither the tail nor a ready
+    page and has no host copy; 2: a tag outside [-1, L) or held by two slots;
+    4: a stamp newer than the clock), and 0 for states that keep them,
+    including their edges (a page without host copy whose rows all sit in the
+    tail, a tag of L - 1, a stamp equal to the clock)."""
+    # H=16, P=4, T=4: tail rows 12..15 (page 3); pages 0 and 2 ready at
+    # physical pages 1 and 0 without host copies; page 1 only on the host
+    src = one_request_source(H=16, P=4, T=4, B=4, page_map=[1, -1, 0, -1],
+                             host_valid=[0, 1, 0, 1], R=16)
+    assert src.check().tolist() == [0]
+
+    def mask():
+        return int(src.check()[0])
+
+    # residency: page 1 loses its host copy -> rows 4..7 are nowhere
+    src.host_valid[0, 1] = 0
+    assert mask() == 1
+    src.host_valid[0, 1] = 1
+    # page 3 without host copy and not ready, but every row in the tail
+    src.host_valid[0, 3] = 0
+    assert mask() == 0
+    # one append moves row 12 out of the tail window: now it is nowhere
+    assert src.append(new_row(src, 16))[0] == orc.OK
+    assert mask() == 1
+    src.host_valid[0, 3] = 1
+    assert mask() == 0
+    # a ready page released without a host copy
+    src.page_map[0, 2] = -1
+    assert mask() == 1
+    src.page_map[0, 2] = 0
+
+    L = int(src.L[0])
+    src.clock[0] = 5
+    src.tag[0] = [3, L - 1, -1, 9]
+    src.stamp[0] = [5, 4, 0, 1]
+    assert mask() == 0
+    for bad in ([3, L, -1, 9], [3, L - 1, -2, 9], [3, 9, -1, 9], [7, L - 1, 7, 9]):
+        src.tag[0] = bad
+        assert mask() == 2, bad
+    src.tag[0] = [3, L - 1, -1, 9]
+    src.stamp[0] = [5, 6, 0, 1]
+    assert mask() == 4
+    src.stamp[0] = [5, 4, 0xFFFFFFFF, 1]   # an empty slot's stamp counts too
+    assert mask() == 4
+    # all three at once
+    src.host_valid[0, 1] = 0
+    src.tag[0] = [3, 3, -1, 9]
+    assert mask() == 7
+
+
+def test_check_residency_bit_on_a_partial_last_page():
+    """A trailing partial page is never ready, so its rows need a host copy
+    once they leave the tail."""
+    src = one_request_source(H=14, P=4, T=2, B=2, page_map=[0, -1, -1, -1],
+                             host_valid=[0, 1, 1, 1], R=16)
+    assert src.check().tolist() == [0]
+    src.host_valid[0, 3] = 0     # rows 12, 13: both in the tail (L = 14, T = 2)
+    assert src.check().tolist() == [0]
+    assert src.append(new_row(src, 14))[0] == orc.OK   # row 12 leaves the tail
+    assert src.check().tolist() == [1]
 
 
 # ----------------------------------------------------------------- textbook LRU
