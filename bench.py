@@ -12,7 +12,11 @@ Prints one JSON line.  `value` is selected rows resolved+gathered per
 second: (request, payload layer, selected row) entries written by the
 gather; rows of layers that only inherit a location vector are not counted.
 
-  python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload c5] [--no-cpu-baseline]
+
+The default workload is the largest: DeepSeek-style long context (64
+requests of 524288-row histories, 4 resolving + 8 Reuse layers, 22 GB pinned
+host store).
 """
 from __future__ import annotations
 
@@ -31,6 +35,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# MI355X's host interface is PCIe 5.0 x16: 128 GB/s both ways, 64 GB/s in
+# one direction (host to device is the direction the fills use)
+HOST_LINK_PEAK_GBS = 64.0
 
 
 def log(msg):
@@ -42,21 +49,24 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=28)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests the CPU baseline runs (a bounded sample of the workload's; "
+                         "requests never interact, so rows/s is per request processed)")
     ap.add_argument("--no-graph", action="store_true",
                     help="issue the timed steps eagerly instead of replaying one HIP graph")
     ap.add_argument("--prefetch-groups", default="2",
                     help="layer groups whose host fills overlap earlier gathers: a count "
                          "(equal groups, 0 = off) or comma-separated group sizes")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "prefetch", "fused"],
+    ap.add_argument("--schedule", default="auto",
+                    choices=["auto", "prefetch", "fused", "pipelined"],
                     help="fused: host fills and the gather of the rows they bring in as one "
-                         "pass beside the gather of all other rows; prefetch: fills in layer "
-                         "groups ahead of per-group gathers; auto: fused for several payload "
-                         "layers sharing the indices, one physical source with several resolving "
-                         "layers (timed eagerly: its graph capture is disabled) or small calls "
-                         "(n_req * sel_cap <= 4096), else prefetch")
+                         "pass beside the gather of all other rows; pipelined: the fused "
+                         "launches on a side stream so that each resolve (the next step's "
+                         "included) runs beside the previous gathers; prefetch: fills in layer "
+                         "groups ahead of per-group gathers; auto: see auto_schedule()")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of the K steps from the same state (median reported)")
     ap.add_argument("--hot-slots", type=int, default=0,
@@ -118,18 +128,28 @@ def auto_fused(cfg) -> bool:
             or cfg.n_req * cfg.sel_cap <= 4096)
 
 
-def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None):
+def auto_schedule(cfg) -> str:
+    """The default schedule: where the fused schedule is the default
+    (auto_fused), its pipelined form, whose resolves leave the critical path;
+    else prefetch."""
+    return "pipelined" if auto_fused(cfg) else "prefetch"
+
+
+def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None, n_reqs=None):
     """The oracle as it stands, on this host's cores (or `threads` of them),
-    over the same decode steps from a fresh state; the pass is repeated (state
-    restored) until at least `min_s` seconds of work, and stops early at
-    `budget_s`."""
+    over the same decode steps from a fresh state, for the first `n_reqs`
+    requests (all by default); the pass is repeated (state restored) until at
+    least `min_s` seconds of work, and stops early at `budget_s`."""
     from oracle.runner import OracleRun
     from synth import Inputs
     inputs = Inputs(cfg, max_new=total_steps)
-    run = OracleRun(inputs, threads=threads)
+    n = cfg.n_req if not n_reqs else min(n_reqs, cfg.n_req)
+    reqs = list(range(n))
+    run = OracleRun(inputs, reqs=reqs, threads=threads)
     src = run.src
     snap = src.snapshot()
-    sels = {s: [inputs.selections(s, g) for g in range(cfg.groups)] for s in range(total_steps)}
+    sels = {s: [inputs.selections(s, g, reqs) for g in range(cfg.groups)]
+            for s in range(total_steps)}
     n_out = cfg.payload_layers if cfg.reuse == "distinct" else 1
     rows = 0
     spent = 0.0
@@ -153,12 +173,14 @@ def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None):
                 break
         spent += time.perf_counter() - t0
         passes += 1
-    # the oracle runs one thread per request shard: at most n_req of them
+    # the oracle runs one thread per request shard: at most n of them
+    which = (f"all {cfg.n_req} requests" if n == cfg.n_req
+             else f"requests 0..{n - 1} of {cfg.n_req}")
     return {"value": round(rows / spent, 1), "unit": "rows/s",
-            "cores": int(min(src.threads, cfg.n_req)),
+            "cores": int(min(src.threads, n)),
             "kind": "oracle",
-            "sample": f"{cfg.name}: {passes} pass(es) over decode steps 0..{total_steps - 1} of all "
-                      f"{cfg.n_req} requests from a fresh state, {steps_done} steps, "
+            "sample": f"{cfg.name}: {passes} pass(es) over decode steps 0..{total_steps - 1} of "
+                      f"{which} from a fresh state, {steps_done} steps, "
                       f"{spent:.1f} s of oracle time"}
 
 
@@ -209,12 +231,14 @@ def traffic_records():
     return out
 
 
-def recorded_traffic(workload, schedule):
-    """HBM bytes per gather launch measured by counters for this workload and
-    schedule on the current gather source, or None."""
+def recorded_traffic(workload, schedule, kernel="gather_kernel"):
+    """Bytes per launch of `kernel` (gather_kernel or fused_gather_kernel)
+    measured by counters for this workload and schedule on the current
+    source of those kernels, or None."""
     source = gather_source_hash()
     for fields in traffic_records():
         if (fields.get("workload") == workload and fields.get("schedule") == schedule
+                and fields.get("kernel", "gather_kernel") == kernel
                 and fields.get("source_sha256") == source):
             try:
                 return int(fields["traffic_bytes_per_launch"])
@@ -440,14 +464,17 @@ def main():
     counts = rows_per_group(inputs, range(W, total))
     pg = args.prefetch_groups
     pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
-    fused = args.schedule == "fused" or (args.schedule == "auto" and auto_fused(cfg))
+    schedule = auto_schedule(cfg) if args.schedule == "auto" else args.schedule
+    pipelined = schedule == "pipelined"
+    fused = schedule in ("fused", "pipelined")
     no_graph = args.no_graph
     if fused and cfg.reuse != "distinct" and not no_graph:
         # its graph capture is disabled (GpuRun.capture): timed eagerly
         log("the fused schedule of one physical source runs eagerly (no graph)")
         no_graph = True
     for s in range(W):
-        gpu.step(s, prefetch_groups=pg, fused=fused)
+        gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+    gpu.finish()
     torch.cuda.synchronize()
     snap = gpu.snapshot()
     stats_before = gpu.stats_dict()
@@ -469,13 +496,15 @@ def main():
         gpu.restore(snap)
         gpu.ctx.timing_begin(64 * K + 64)
         for s in range(W, total):
-            gpu.step(s, prefetch_groups=pg, fused=fused)
+            gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+        gpu.finish()
         fused_runs = launch_means_ms(gpu.ctx.timing_end()).get("fused", [])
         torch.cuda.synchronize()
         launches["fused"] = fused_runs
     if not no_graph:
         gpu.restore(snap)
-        graph = gpu.capture(range(W, total), prefetch_groups=pg, fused=fused)
+        graph = gpu.capture(range(W, total), prefetch_groups=pg, fused=fused,
+                            pipelined=pipelined)
         torch.cuda.synchronize()
         log("captured the timed steps into one graph")
 
@@ -515,7 +544,8 @@ def main():
         start.record()
         if no_graph:
             for s in range(W, total):
-                gpu.step(s, prefetch_groups=pg, fused=fused)
+                gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+            gpu.finish()
         else:
             graph.replay()
         end.record()
@@ -536,46 +566,46 @@ def main():
 
     stats_all = gpu.stats_dict()
     stats = {kk: stats_all[kk] - stats_before[kk] for kk in stats_all}
-    # gather roofline: algorithmic bytes per launch = rows * (R read + R write) per
-    # payload layer + one 4-byte location word per row.  In the fused schedule
-    # the gather kernel moves the resident rows (tail, page, hot hit) and reads
-    # every location word; the rows copied from host go through the fill pass.
+    # Algorithmic bytes per launch (rows already resident in HBM and pinned
+    # host memory when timing starts):
+    #   gather (all rows, or the resident rows of the fused schedule): each
+    #     moved row R read + R written per payload layer, plus one 4-byte
+    #     location word per entry;
+    #   fused launch: every entry's row written to the output (2R per layer
+    #     in HBM: a resident row is read and written; a fresh row crosses the
+    #     host link once, R, and is written to its hot slot and the output),
+    #     plus the location word of every entry and the selection entry of
+    #     every fresh one;
+    #   refill: each filled row R over the host link and R written, per layer.
+    entries = sum(counts.values())
+    fresh = stats["miss"]
     g_list = launches.get("gather", [])
     gather_calls = len(g_list)
-    entries = sum(counts.values())
-    moved = entries - stats["miss"] if fused else entries
+    moved = entries - fresh if fused else entries
     bytes_gather = (moved * 2 * cfg.R * n_out + entries * 4) / max(1, gather_calls)
     g_ms = sum(g_list) / max(1, gather_calls)
-    achieved = bytes_gather / (g_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(cfg.name, "fused" if fused
-                                            else f"prefetch:{args.prefetch_groups}"),
-                "kernel": "gather_kernel<resident>" if fused else "gather_kernel<all>",
-                "bytes_per_launch": int(bytes_gather),
-                "launch_us": round(g_ms * 1e3, 2),
-                "timing": ("start/end events of each gather dispatch (hipExtLaunchKernel) in an "
-                           "eager pass over the same timed steps from the same starting state, "
-                           "no two kernels overlapping"
-                           + ("; the timed pass runs this gather as the resident part of one "
-                              "fused launch with the fill, which is issued here as its two "
-                              "halves so that each runs alone"
-                              if fused else
-                              ", with the same launches as the timed pass"))}
+    g_gbs = bytes_gather / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
+    dev_copy = device_copy_gbs(torch)
+    gather_alone = {"kernel": "gather_kernel<resident>" if fused else "gather_kernel<all>",
+                    "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(cfg.name, "fused" if fused
+                                                else f"prefetch:{args.prefetch_groups}"),
+                    "bytes_per_launch": int(bytes_gather), "launch_us": round(g_ms * 1e3, 2),
+                    "device_copy_gbs": round(dev_copy, 1),
+                    "frac_of_device_copy": round(g_gbs / dev_copy, 4),
+                    "timing": "start/end events of each gather dispatch (hipExtLaunchKernel) in "
+                              "an eager pass over the same timed steps from the same starting "
+                              "state, no two kernels overlapping"
+                              + ("; in the timed pass this gather is the resident part of the "
+                                 "fused launch" if fused else "")}
 
-    found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
-    split = {"step1_tail_or_page": round((stats["tail"] + stats["page"]) / found, 4),
-             "step2_hot_hit": round(stats["hit"] / found, 4),
-             "step3_host": round(stats["miss"] / found, 4)}
-    per_call_us = {name: round(sum(v) / len(v) * 1e3, 2) for name, v in launches.items()}
     # host refill path: every fill is fetched once per payload layer (all layers
     # replay the fills for shared indices with distinct payloads)
     fill_layers = cfg.payload_layers if cfg.reuse == "distinct" else 1
     host_bytes = stats["fill"] * cfg.R * fill_layers
     fill_calls = launches.get("refill", [])
     fill_s = sum(fill_calls) * 1e-3
-    roofline["device_copy_gbs"] = round(device_copy_gbs(torch), 1)
-    roofline["frac_of_device_copy"] = round(achieved / roofline["device_copy_gbs"], 4)
     copy_gbs = host_link_gbs(torch)
     seq_gbs = zero_copy_read_gbs(torch, gpu)
     link = max(copy_gbs, seq_gbs)
@@ -586,13 +616,62 @@ def main():
                  "frac": round(refill_gbs / link, 4) if refill_gbs else None,
                  "host_bytes_per_step": int(host_bytes / K),
                  "refill_calls_per_step": len(fill_calls) / K}
+
+    # The roofline is that of the kernel that takes most of the timed pass.
+    if fused:
+        f_list = launches.get("fused", [])
+        n_launch = max(1, len(f_list))
+        d_ms = sum(f_list) / n_launch
+        d_host = n_out * fresh * cfg.R / n_launch
+        d_hbm = (n_out * entries * 2 * cfg.R + entries * 4 + fresh * 4) / n_launch
+        d_kernel = "fused_gather_kernel"
+        d_timing = ("start/end events of each fused dispatch in an eager pass of the timed "
+                    "pass's own launches (same streams and overlaps) over the same steps from "
+                    "the same starting state")
+    elif fill_calls and sum(fill_calls) >= sum(g_list):
+        n_launch = len(fill_calls)
+        d_ms = fill_s * 1e3 / n_launch
+        d_host = host_bytes / n_launch
+        d_hbm = (host_bytes + stats["fill"] * 8 * fill_layers) / n_launch
+        d_kernel = "refill_kernel"
+        d_timing = ("start/end events of each refill dispatch in an eager pass over the same "
+                    "timed steps from the same starting state, no two kernels overlapping")
+    else:
+        n_launch, d_ms, d_host, d_hbm = gather_calls, g_ms, 0.0, bytes_gather
+        d_kernel, d_timing = gather_alone["kernel"], gather_alone["timing"]
+    d_s = max(d_ms, 1e-9) * 1e-3
+    hbm_gbs = d_hbm / d_s / 1e9
+    host_gbs = d_host / d_s / 1e9
+    hbm_part = {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(d_hbm)}
+    if d_host > 0:
+        roofline = {"bound": "host_link", "achieved": round(host_gbs, 1),
+                    "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(cfg.name, "fused" if fused else
+                                                f"prefetch:{args.prefetch_groups}", d_kernel),
+                    "kernel": d_kernel, "bytes_per_launch": int(d_host),
+                    "launch_us": round(d_ms * 1e3, 2), "launches": n_launch,
+                    "measured_link_gbs": round(link, 1),
+                    "frac_of_measured_link": round(host_gbs / link, 4),
+                    "hbm": hbm_part, "timing": d_timing}
+    else:
+        roofline = dict(hbm_part, bound="hbm", kernel=d_kernel, launch_us=round(d_ms * 1e3, 2),
+                        launches=n_launch, traffic=gather_alone["traffic"], timing=d_timing)
+    roofline["gather_alone"] = gather_alone
+
+    found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
+    split = {"step1_tail_or_page": round((stats["tail"] + stats["page"]) / found, 4),
+             "step2_hot_hit": round(stats["hit"] / found, 4),
+             "step3_host": round(stats["miss"] / found, 4)}
+    per_call_us = {name: round(sum(v) / len(v) * 1e3, 2) for name, v in launches.items()}
     line = {
         "metric": "selected rows resolved+gathered/sec and achieved HBM GB/s (% of peak), 1 GPU",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(wall_s * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
         "repeats": len(walls), "ms_per_step_runs": [round(w * 1e3 / K, 4) for w in walls],
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-        "config": {"workload": cfg.name, "schedule": "fused" if fused else "prefetch",
+        "config": {"workload": cfg.name, "schedule": schedule,
                    "prefetch_groups": None if fused else args.prefetch_groups,
                    "launch": "eager" if no_graph else "hip_graph", "n_req": cfg.n_req, "history_rows": cfg.H,
                    "row_bytes": cfg.R, "page_rows": cfg.P, "tail_rows": cfg.T,
@@ -610,9 +689,11 @@ def main():
     gpu.close()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
-        line["cpu_baseline"] = cpu_baseline(cfg, total, args.cpu_budget_s)
+        line["cpu_baseline"] = cpu_baseline(cfg, total, args.cpu_budget_s,
+                                            n_reqs=args.cpu_requests)
         line["cpu_baseline"]["cpu_model"] = cpu_model()
-        one = cpu_baseline(cfg, total, args.cpu_budget_s / 2, min_s=4.0, threads=1)
+        one = cpu_baseline(cfg, total, args.cpu_budget_s / 2, min_s=4.0, threads=1,
+                           n_reqs=args.cpu_requests)
         line["cpu_baseline"]["single_core"] = {"value": one["value"], "unit": one["unit"],
                                                "sample": one["sample"]}
     print(json.dumps(line), flush=True)

@@ -20,6 +20,13 @@
 //             first workgroups of the grid are fill workers, the rest gather
 //             resident tiles, so the two share the chip without the
 //             cross-queue waits that two concurrent launches need.
+//             It may also complete deferred appends (the decoded row of
+//             each entry, whose host copy and length a resolve launch has
+//             already written): a few workgroups write each appended row
+//             into its tail slot, and resident tiles read a tail word naming
+//             that slot from the new rows instead, so no tile reads the slot
+//             while it is written.  The row it replaces left the tail window
+//             with the append, so no word of this launch names it.
 #include "kvr_internal.h"
 #include "rows.h"
 
@@ -45,6 +52,9 @@ struct GatherArgs {
     int32_t stride;
     int32_t *status;
     int32_t fill_tile;        // entries per fill job (at most kFillTile)
+    int32_t n;                // request entries of the call
+    const uint8_t *new_rows;  // deferred appends: [context layers][n][R], or null
+    const int32_t *append_pos;  // [n] appended position per entry, -1 for none
 };
 
 // Source of a word in the all and resident modes (null: nothing to copy).
@@ -87,7 +97,15 @@ __device__ __forceinline__ void gather_tile(const GatherArgs &a, int x, int i, i
     if ((int)threadIdx.x < nrows) {
         const uint32_t w = a.loc[(int64_t)i * a.stride + j0 + threadIdx.x];
         bool bad;
-        sSrc[threadIdx.x] = resident_src(a, lp, r, w, MODE == kGatherResident, bad);
+        const uint8_t *src = resident_src(a, lp, r, w, MODE == kGatherResident, bad);
+        if (a.append_pos && src && (w >> kPlaceShift) == KVR_PLACE_TAIL) {
+            // the slot of a deferred append is being written in this launch:
+            // its row comes from the new rows
+            const int32_t apos = a.append_pos[i];
+            if (apos >= 0 && (w & kIndexMask) == (uint32_t)(apos % a.sh.T))
+                src = a.new_rows + ((int64_t)a.layer[t] * a.n + i) * R;
+        }
+        sSrc[threadIdx.x] = src;
         if (bad && a.status)
             a.status[i] = KVR_E_RANGE;
     }
@@ -238,9 +256,30 @@ __global__ __launch_bounds__(NT) void fill_kernel(GatherArgs a, int32_t n, int32
     fill_jobs(a, blockIdx.y, blockIdx.x, gridDim.x, n, tiles_per_req, fl);
 }
 
+// The appended row of entry i of every target layer into its tail slot
+// (deferred appends), by one workgroup.
+__device__ __forceinline__ void write_appended(const GatherArgs &a, int i, int nt)
+{
+    const int32_t apos = a.append_pos[i];
+    const int r = a.req_ids ? a.req_ids[i] : i;
+    if (apos < 0 || a.sh.T <= 0 || r < 0 || r >= a.sh.n_req)
+        return;
+    const int R = a.sh.R;
+    const int C = R / 16;
+    for (int c = threadIdx.x; c < nt * C; c += NT) {
+        const int t = c / C;
+        const int off = (c - t * C) * 16;
+        const int l = a.layer[t];
+        u32x4 v;
+        load_chunk(v, a.new_rows + ((int64_t)l * a.n + i) * R + off);
+        store_chunk(a.layers[l].tail + ((int64_t)r * a.sh.T + apos % a.sh.T) * R + off, v);
+    }
+}
+
 // Fill and resident gather in one 1-D grid: workgroups [0, nt * workers) are
-// the fill workers of every target (so all of them start first), the rest
-// are resident tiles, x fastest, then request entry, then target.
+// the fill workers of every target (so all of them start first), then, with
+// deferred appends, one workgroup per request entry writes its appended rows,
+// the rest are resident tiles, x fastest, then request entry, then target.
 __global__ __launch_bounds__(NT) void fused_gather_kernel(GatherArgs a, int32_t n,
                                                           int32_t tiles_per_req, int32_t workers,
                                                           int32_t nt, int32_t tiles_x)
@@ -251,10 +290,13 @@ __global__ __launch_bounds__(NT) void fused_gather_kernel(GatherArgs a, int32_t 
     } sm;
     const int64_t b = blockIdx.x;
     const int64_t n_fill = (int64_t)workers * nt;
+    const int64_t n_app = a.append_pos ? n : 0;
     if (b < n_fill) {
         fill_jobs(a, (int)(b / workers), (int)(b % workers), workers, n, tiles_per_req, sm.fill);
+    } else if (b < n_fill + n_app) {
+        write_appended(a, (int)(b - n_fill), nt);
     } else {
-        const int64_t g = b - n_fill;
+        const int64_t g = b - n_fill - n_app;
         const int64_t per_t = (int64_t)tiles_x * n;
         const int t = (int)(g / per_t);
         const int64_t rem = g - (int64_t)t * per_t;
@@ -267,7 +309,7 @@ __global__ __launch_bounds__(NT) void fused_gather_kernel(GatherArgs a, int32_t 
 hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *targets,
                          int32_t n_targets, int32_t n, const int32_t *req_ids, const uint32_t *loc,
                          const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,
-                         hipStream_t s)
+                         hipStream_t s, const uint8_t *new_rows, const int32_t *append_pos)
 {
     GatherArgs a;
     a.sh = c->shape;
@@ -279,6 +321,10 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
     a.sel = sel;
     a.stride = stride;
     a.status = status;
+    a.n = n;
+    const bool deferred = mode == kGatherFused && append_pos != nullptr && new_rows != nullptr;
+    a.new_rows = deferred ? new_rows : nullptr;
+    a.append_pos = deferred ? append_pos : nullptr;
     for (int32_t t0 = 0; t0 < n_targets; t0 += kGatherLayersPerLaunch) {
         const int nt = n_targets - t0 < kGatherLayersPerLaunch ? n_targets - t0 : kGatherLayersPerLaunch;
         for (int t = 0; t < nt; ++t) {
@@ -302,7 +348,7 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
             dim3 fgrid((unsigned)workers, nt);
             e = launch(c, KVR_KERNEL_REFILL, fill_kernel, fgrid, dim3(NT), 0, s, a, n, tiles_per_req);
         } else if (mode == kGatherFused) {
-            const int64_t blocks = workers * nt + (int64_t)tiles_x * n * nt;
+            const int64_t blocks = workers * nt + (deferred ? n : 0) + (int64_t)tiles_x * n * nt;
             if (blocks > 0x7FFFFFFF)
                 return hipErrorInvalidConfiguration;
             e = launch(c, KVR_KERNEL_FUSED, fused_gather_kernel, dim3((unsigned)blocks), dim3(NT), 0,

@@ -318,7 +318,8 @@ int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void 
 static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
                          int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
                          int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
-                         int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream)
+                         int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream,
+                         int32_t *append_pos = nullptr)
 {
     if (int rc = check_ctx(ctx))
         return rc;
@@ -345,7 +346,8 @@ static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const 
         return ok();
     hipError_t e = kvr::launch_resolve(ctx, n, req_ids, sel, sel_count, stride, loc, fills,
                                        fill_count, status, stats, fill_layer >= 0 ? 1 : 0,
-                                       static_cast<const uint8_t *>(new_rows), append_status, s);
+                                       static_cast<const uint8_t *>(new_rows), append_status,
+                                       append_pos, s);
     if (e != hipSuccess)
         return hip_fail(e, "resolve launch");
     if (fill_layer >= 0) {
@@ -376,10 +378,24 @@ int kvr_append_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, con
                          fills, fill_count, fill_layer, status, stats, stream);
 }
 
+int kvr_append_resolve_rows_deferred(kvr_ctx *ctx, int32_t n, const int32_t *req_ids,
+                                     const void *new_rows, int32_t *append_status,
+                                     int32_t *append_pos, const int32_t *sel,
+                                     const int32_t *sel_count, int32_t stride, uint32_t *loc,
+                                     kvr_fill *fills, int32_t *fill_count, int32_t fill_layer,
+                                     int32_t *status, kvr_stats *stats, void *stream)
+{
+    if (n > 0 && (!new_rows || !append_pos))
+        return fail(KVR_E_ARG, "new_rows and append_pos are required");
+    return resolve_entry(ctx, n, req_ids, new_rows, append_status, sel, sel_count, stride, loc,
+                         fills, fill_count, fill_layer, status, stats, stream, append_pos);
+}
+
 static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
                         int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
                         const int32_t *count, int32_t stride, void *const *out, int32_t *status,
-                        void *stream)
+                        void *stream, const void *new_rows = nullptr,
+                        const int32_t *append_pos = nullptr)
 {
     if (int rc = check_ctx(ctx, false))
         return rc;
@@ -397,11 +413,29 @@ static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
         if (!out[t] && n > 0 && stride > 0)
             return fail(KVR_E_ARG, "out[%d] is null", t);
     }
+    const bool deferred = append_pos != nullptr;
+    if (deferred) {
+        // the appended rows go to the tail of every payload layer: the call
+        // must name each layer of the context once
+        if (!ctx->meta_bound)
+            return fail(KVR_E_ARG, "metadata not bound");
+        if (n > 0 && !new_rows)
+            return fail(KVR_E_ARG, "new_rows is required");
+        if (n_layers != ctx->cfg.n_layers)
+            return fail(KVR_E_ARG, "deferred appends need all %d layers, got %d",
+                        ctx->cfg.n_layers, n_layers);
+        for (int32_t t = 1; t < n_layers; ++t)
+            for (int32_t u = 0; u < t; ++u)
+                if (layers[u] == layers[t])
+                    return fail(KVR_E_ARG, "layer %d named twice", layers[t]);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     int rc = check_stream(ctx, s);
-    // one launch per group of up to kGatherLayersPerLaunch layers
+    // one launch per group of up to kGatherLayersPerLaunch layers (with
+    // deferred appends a launch runs even for an empty selection: it still
+    // writes the appended rows)
     kvr::GatherTarget targets[kvr::kGatherLayersPerLaunch];
-    for (int32_t t0 = 0; rc == KVR_OK && n > 0 && stride > 0 && t0 < n_layers;
+    for (int32_t t0 = 0; rc == KVR_OK && n > 0 && (stride > 0 || deferred) && t0 < n_layers;
          t0 += kvr::kGatherLayersPerLaunch) {
         const int32_t nt = n_layers - t0 < kvr::kGatherLayersPerLaunch
                                ? n_layers - t0 : kvr::kGatherLayersPerLaunch;
@@ -410,7 +444,8 @@ static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
             targets[t].out = static_cast<uint8_t *>(out[t0 + t]);
         }
         hipError_t e = kvr::launch_gather(ctx, mode, targets, nt, n, req_ids, loc, sel, count, stride,
-                                          status, s);
+                                          status, s, static_cast<const uint8_t *>(new_rows),
+                                          append_pos);
         if (e != hipSuccess)
             rc = hip_fail(e, "gather launch");
     }
@@ -453,6 +488,20 @@ int kvr_fused_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers,
         return fail(KVR_E_ARG, "sel is required");
     return gather_entry(ctx, kvr::kGatherFused, n_layers, layers, n, req_ids, loc, sel, count,
                         stride, out, status, stream);
+}
+
+int kvr_fused_gather_append_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                                 const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                                 const int32_t *count, int32_t stride, void *const *out,
+                                 int32_t *status, const void *new_rows, const int32_t *append_pos,
+                                 void *stream)
+{
+    if (n > 0 && stride > 0 && n_layers > 0 && !sel)
+        return fail(KVR_E_ARG, "sel is required");
+    if (n > 0 && !append_pos)
+        return fail(KVR_E_ARG, "append_pos is required");
+    return gather_entry(ctx, kvr::kGatherFused, n_layers, layers, n, req_ids, loc, sel, count,
+                        stride, out, status, stream, new_rows, append_pos);
 }
 
 int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,

@@ -110,11 +110,13 @@ hipError_t launch(const kvr_ctx *c, int32_t kind, void (*kernel)(P...), dim3 gri
 // Launchers (return a hipError_t of the launch).
 // new_rows non-null: the append of kvr_append_rows for the same requests runs
 // first, in the same launch (append_status as its status, may be null).
+// append_pos non-null: the append is deferred (host row and L only; the tail
+// slot is left to a gather launch) and append_pos receives the positions.
 hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, const int32_t *sel,
                           const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
                           int32_t *fill_count, int32_t *status, kvr_stats *stats,
                           int32_t count_host_bytes, const uint8_t *new_rows,
-                          int32_t *append_status, hipStream_t s);
+                          int32_t *append_status, int32_t *append_pos, hipStream_t s);
 size_t resolve_lds_bytes(const Shape &sh);
 hipError_t prepare_resolve_kernel();
 
@@ -132,10 +134,15 @@ constexpr int32_t kGatherAll = 0;       // every valid word
 constexpr int32_t kGatherResident = 1;  // every valid word but fresh hot-cache rows
 constexpr int32_t kGatherFill = 2;      // fresh hot-cache rows, from host into slot and out
 constexpr int32_t kGatherFused = 3;     // fill and resident in one launch
+// new_rows/append_pos non-null (fused mode only): the launch also completes
+// deferred appends of the same entries: it writes each appended row of every
+// target layer into its tail slot and serves tail words naming that slot
+// from new_rows.
 hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *targets,
                          int32_t n_targets, int32_t n, const int32_t *req_ids, const uint32_t *loc,
                          const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,
-                         hipStream_t s);
+                         hipStream_t s, const uint8_t *new_rows = nullptr,
+                         const int32_t *append_pos = nullptr);
 
 hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,
                          const uint8_t *new_rows, int32_t *status, hipStream_t s);

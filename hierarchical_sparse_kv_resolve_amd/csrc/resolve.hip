@@ -82,6 +82,11 @@ struct ResolveArgs {
     const LayerPtrs *layers;
     const uint8_t *new_rows;
     int32_t *append_status;
+    // deferred append: the host row and L only; the tail slot is written by
+    // the gather launch that consumes append_pos (the appended position, or
+    // -1 when the entry appended nothing)
+    int32_t *append_pos;
+    int32_t defer_tail;
 };
 
 __device__ __forceinline__ int hslot(int32_t key, int hs)
@@ -181,11 +186,12 @@ __device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const in
 
 // The request's decoded row of every layer into tail slot L mod T and, written
 // through, host row L (what kvr_append_rows does), by all threads of the block.
+// A deferred append writes the host row only.
 __device__ __forceinline__ void append_row(const ResolveArgs &a, int i, int r, int32_t L)
 {
     const Shape &sh = a.sh;
     const int C = sh.R / 16;
-    const int per_layer = C * (sh.T > 0 ? 2 : 1);
+    const int per_layer = C * (sh.T > 0 && !a.defer_tail ? 2 : 1);
     for (int c = threadIdx.x; c < per_layer * sh.n_layers; c += NT) {
         const int l = c / per_layer;
         const int e = c - l * per_layer;
@@ -262,6 +268,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a)
         }
         if (tid == 0 && a.append_status)
             a.append_status[i] = code;
+        if (tid == 0 && a.append_pos)
+            a.append_pos[i] = appended ? L - 1 : -1;
     }
     if (!r_ok || k < 0 || k > a.stride) {
         if (appended) {
@@ -932,12 +940,14 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
                           const int32_t *sel_count, int32_t stride, uint32_t *loc, kvr_fill *fills,
                           int32_t *fill_count, int32_t *status, kvr_stats *stats,
                           int32_t count_host_bytes, const uint8_t *new_rows,
-                          int32_t *append_status, hipStream_t s)
+                          int32_t *append_status, int32_t *append_pos, hipStream_t s)
 {
     ResolveArgs a;
     a.layers = c->layers_d;
     a.new_rows = new_rows;
     a.append_status = append_status;
+    a.append_pos = append_pos;
+    a.defer_tail = append_pos != nullptr;
     a.sh = c->shape;
     a.L = c->L;
     a.page_map = c->page_map;

@@ -33,7 +33,7 @@ REUSE_DISTINCT_PAYLOAD = 1
 # Every entry point of include/kvr.h.
 EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
            "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_append_resolve_rows",
-           "kvr_gather_rows",
+           "kvr_append_resolve_rows_deferred", "kvr_gather_rows", "kvr_fused_gather_append_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
            "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
            "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
@@ -86,10 +86,12 @@ def lib():
             "kvr_append_rows": [P, I, P, P, P, P],
             "kvr_resolve_rows": [P, I, P, P, P, I, P, P, P, I, P, P, P],
             "kvr_append_resolve_rows": [P, I, P, P, P, P, P, I, P, P, P, I, P, P, P],
+            "kvr_append_resolve_rows_deferred": [P, I, P, P, P, P, P, P, I, P, P, P, I, P, P, P],
             "kvr_gather_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_gather_resident_rows": [P, I, P, I, P, P, P, I, P, P, P],
             "kvr_fill_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
             "kvr_fused_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
+            "kvr_fused_gather_append_rows": [P, I, P, I, P, P, P, P, I, P, P, P, P, P],
             "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
             "kvr_reuse_locations": [P, I, I, P, I, P, P, P, P, I, P, P, P, P],
             "kvr_status_summary": [P, I, P],
@@ -296,6 +298,18 @@ class Context:
                                              stride, lc, fl, fc, fill_layer, st, sts,
                                              _stream(stream)))
 
+    def append_resolve_rows_deferred(self, n, req_ids, new_rows, append_status, append_pos, sel,
+                                     sel_count, stride, loc, fills, fill_count, fill_layer,
+                                     status, stats=None, stream=None):
+        NL, R = self.cfg.n_layers, self.cfg.row_bytes
+        rid, sl, sc, lc, fl, fc, st, sts = self._resolve_args(n, req_ids, sel, sel_count, stride,
+                                                              loc, fills, fill_count, status,
+                                                              stats)
+        _check(lib().kvr_append_resolve_rows_deferred(
+            self.handle, n, rid, _dev(new_rows, "new_rows", NL * n * R),
+            _dev(append_status, "append_status", 4 * n), _dev(append_pos, "append_pos", 4 * n),
+            sl, sc, stride, lc, fl, fc, fill_layer, st, sts, _stream(stream)))
+
     def _gather_args(self, layers, n, req_ids, loc, count, stride, outs, status):
         nl = len(layers)
         m = max(n, 0) * max(stride, 0)
@@ -335,6 +349,17 @@ class Context:
         sl = _dev(sel, "sel", 4 * max(n, 0) * max(stride, 0))
         _check(lib().kvr_fused_gather_rows(self.handle, nl, arr_l, n, rid, lc, sl, cnt, stride,
                                            arr_o, st, _stream(stream)))
+
+    def fused_gather_append_rows(self, layers, n, req_ids, loc, sel, count, stride, outs,
+                                 new_rows, append_pos, status=None, stream=None):
+        nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(layers, n, req_ids, loc, count,
+                                                               stride, outs, status)
+        sl = _dev(sel, "sel", 4 * max(n, 0) * max(stride, 0))
+        NL, R = self.cfg.n_layers, self.cfg.row_bytes
+        _check(lib().kvr_fused_gather_append_rows(
+            self.handle, nl, arr_l, n, rid, lc, sl, cnt, stride, arr_o, st,
+            _dev(new_rows, "new_rows", NL * n * R), _dev(append_pos, "append_pos", 4 * n),
+            _stream(stream)))
 
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
         m = max(n, 0) * max(q, 0) * max(k, 0)

@@ -93,21 +93,58 @@ class GpuRun:
                                 self.pool[l] if cfg.pool_pages else None, self.hot[l], ptr)
         self.ctx.init_state()
         G, cap = cfg.groups, cfg.sel_cap
-        self.loc = [torch.empty((n, cap), dtype=i32, device=dev) for _ in range(G)]
-        self.fills = [torch.empty((n, cfg.B, 2), dtype=i32, device=dev) for _ in range(G)]
-        self.fill_count = [torch.empty(n, dtype=i32, device=dev) for _ in range(G)]
-        self.status = [torch.empty(n, dtype=i32, device=dev) for _ in range(G)]
+        # The per-call outputs of a step (locations, fills, status, verify
+        # union, appended positions).  With one resolving layer per step two
+        # sets alternate by step parity, so that in the pipelined schedule
+        # the next step's resolve does not overwrite what this step's gather
+        # still reads; with several resolving layers each layer's set is
+        # rewritten only a whole step later.  The attributes below always
+        # name the set of the step issued last.
+        self._nbuf = 2 if G == 1 else 1
+        self._sets = []
+        for _ in range(self._nbuf):
+            bs = {"loc": [torch.empty((n, cap), dtype=i32, device=dev) for _ in range(G)],
+                  "fills": [torch.empty((n, cfg.B, 2), dtype=i32, device=dev) for _ in range(G)],
+                  "fill_count": [torch.empty(n, dtype=i32, device=dev) for _ in range(G)],
+                  "status": [torch.empty(n, dtype=i32, device=dev) for _ in range(G)],
+                  "append_pos": torch.empty(n, dtype=i32, device=dev)}
+            if cfg.q > 1:
+                bs.update(union=torch.empty((n, cfg.q * cfg.k), dtype=i32, device=dev),
+                          union_count=torch.empty(n, dtype=i32, device=dev),
+                          map=torch.empty((n, cfg.q, cfg.k), dtype=i32, device=dev))
+            self._sets.append(bs)
+        self._use_set(0)
         self.append_status = torch.empty(n, dtype=i32, device=dev)
         self.gather_status = torch.zeros(n, dtype=i32, device=dev)
         self.stats = torch.zeros(len(kvr.STATS_FIELDS), dtype=torch.int64, device=dev)
-        if cfg.q > 1:
-            self.union = torch.empty((n, cfg.q * cfg.k), dtype=i32, device=dev)
-            self.union_count = torch.empty(n, dtype=i32, device=dev)
-            self.map = torch.empty((n, cfg.q, cfg.k), dtype=i32, device=dev)
         n_out = nl if cfg.reuse == "distinct" else 1
         self.outs = [[torch.full((n, cap, cfg.R), 0xEE, dtype=torch.uint8, device=dev)
                       for _ in range(n_out)] for _ in range(G)]
         self.sel_dev, self.rows_dev = {}, {}
+        # Every stream a schedule may use exists before any step is issued or
+        # captured, and the events a step records stay referenced until the
+        # step (or a whole capture) is done, so no stream or event is created
+        # or destroyed while a capture is open.
+        self._side_streams = {k: torch.cuda.Stream() for k in (1, 2)}  # default priority
+        self._events = []
+        # pipelined schedule: the side-stream event after the last gather
+        # that read each (buffer set, group), and after the last side launch
+        self._gather_done = {}
+        self._side_last = None
+
+    def _use_set(self, b: int):
+        bs = self._sets[b]
+        self.loc, self.fills = bs["loc"], bs["fills"]
+        self.fill_count, self.status = bs["fill_count"], bs["status"]
+        self.append_pos = bs["append_pos"]
+        if self.cfg.q > 1:
+            self.union, self.union_count, self.map = bs["union"], bs["union_count"], bs["map"]
+
+    def finish(self, stream=None):
+        """Make `stream` (default: the current one) wait for the side-stream
+        work of the pipelined schedule issued so far.  No host wait."""
+        if self._side_last is not None:
+            (stream or self.torch.cuda.current_stream()).wait_event(self._side_last)
 
     def close(self):
         self.torch.cuda.synchronize()
@@ -128,9 +165,23 @@ class GpuRun:
                                for x in gs]
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
-    def step(self, s: int, prefetch_groups=0, serialize: bool = False, fused: bool = False):
+    def step(self, s: int, prefetch_groups=0, serialize: bool = False, fused: bool = False,
+             pipelined: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
+
+        pipelined=True (with fused=True, not serialized): the fused schedule
+        with every fused launch on a side stream and every resolve on the
+        current stream, and nothing joining the two at the end of a step, so
+        that the next step's resolve runs while this step's last fused launch
+        gathers.  The step's append is deferred (append_resolve_rows_deferred
+        writes the host copy and the length) and completed by the step's
+        first fused launch (fused_gather_append_rows), because the tail slot
+        it overwrites may still be read by the previous step's gather.  A
+        resolve waits only for the gather that last read its output buffers.
+        Call finish() before work on the current stream that needs this
+        step's gathered rows or hot payload (capture() and the read-back
+        helpers do).
 
         prefetch_groups = 0: resolve fills payload layer 0 from host, one
         replay call fills the other layers, one gather call covers them all.
@@ -159,6 +210,18 @@ class GpuRun:
         on each other's events)."""
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
+        if not getattr(self, "_capturing", False):
+            # the previous step's events (those later steps of the pipelined
+            # schedule wait on stay referenced by _gather_done / _side_last)
+            self._events = []
+        self._use_set(s % self._nbuf)
+        if pipelined:
+            if not fused or serialize or not self.fuse_append:
+                raise ValueError("the pipelined schedule is the fused one, not serialized, "
+                                 "with the append inside the first resolve")
+            self._step_pipelined(s)
+            return
+        self.finish()  # other schedules start from a joined side stream
         main = torch.cuda.current_stream()
         last_filled = last_resident = None
         if not self.fuse_append:
@@ -192,7 +255,7 @@ class GpuRun:
                 # layer's fill comes after this layer's resident gather (its
                 # victims may be slots that gather reads) and its resident
                 # gather after this fill (its hits may be slots the fill wrote).
-                resolved = torch.cuda.Event()
+                resolved = self._event()
                 resolved.record(main)
                 side = self._side()
                 side.wait_event(resolved)
@@ -202,11 +265,11 @@ class GpuRun:
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
                                         stride, stream=main)
                 if g == cfg.groups - 1:
-                    done = torch.cuda.Event()
+                    done = self._event()
                     done.record(side)
                     main.wait_event(done)
             elif fused:
-                resolved = torch.cuda.Event()
+                resolved = self._event()
                 resolved.record(main)
                 side = self._side()
                 side.wait_event(resolved)
@@ -216,7 +279,7 @@ class GpuRun:
                     side.wait_event(last_resident)
                 ctx.fill_gather_rows(layers, n, None, loc, src, count, stride, outs,
                                      self.gather_status, stream=side)
-                filled = torch.cuda.Event()
+                filled = self._event()
                 filled.record(side)
                 res = main if cfg.reuse == "distinct" else self._side(2)
                 res.wait_event(resolved)
@@ -226,7 +289,7 @@ class GpuRun:
                     res.wait_event(last_filled)
                 ctx.gather_resident_rows(layers, n, None, loc, count, stride, outs,
                                          self.gather_status, stream=res)
-                resident = torch.cuda.Event()
+                resident = self._event()
                 resident.record(res)
                 last_filled, last_resident = filled, resident
                 for _ in range(1, cfg.layers_per_group):
@@ -241,7 +304,7 @@ class GpuRun:
                 # (resolve touches metadata only).  The side stream keeps the
                 # next fill behind this gather: its victims may be slots this
                 # gather still reads.
-                resolved = torch.cuda.Event()
+                resolved = self._event()
                 resolved.record(main)
                 side = self._side()
                 side.wait_event(resolved)
@@ -253,7 +316,7 @@ class GpuRun:
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
                                         stride, stream=side)
                 if g == cfg.groups - 1 or serialize:
-                    done = torch.cuda.Event()
+                    done = self._event()
                     done.record(side)
                     main.wait_event(done)
             elif cfg.reuse != "distinct":
@@ -274,7 +337,7 @@ class GpuRun:
                                 self.outs[g], self.gather_status, stream=main)
             else:
                 groups = layer_groups(self.nl, prefetch_groups)
-                resolved = torch.cuda.Event()
+                resolved = self._event()
                 resolved.record(main)
                 side = self._side()
                 side.wait_event(resolved)
@@ -282,7 +345,7 @@ class GpuRun:
                 for grp in groups:
                     ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, grp.tolist(), n, None,
                                         loc, None, count, stride, fills, fc, stream=side)
-                    ev = torch.cuda.Event()
+                    ev = self._event()
                     ev.record(side)
                     ready.append(ev)
                 if serialize:
@@ -292,6 +355,53 @@ class GpuRun:
                     ctx.gather_rows(grp.tolist(), n, None, loc, count, stride,
                                     [self.outs[g][l] for l in grp], self.gather_status,
                                     stream=main)
+
+    def _step_pipelined(self, s: int):
+        torch = self.torch
+        cfg, ctx, n = self.cfg, self.ctx, self.n
+        main, side = torch.cuda.current_stream(), self._side()
+        b = s % self._nbuf
+        distinct = cfg.reuse == "distinct"
+        layers = list(range(self.nl)) if distinct else [0]
+        for g in range(cfg.groups):
+            sel = self.sel_dev[s][g]
+            k = sel.shape[-1]
+            free = self._gather_done.get((b, g))
+            if free is not None:
+                main.wait_event(free)  # the gather that last read this set's buffers
+            if cfg.q > 1:
+                ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
+                                            self.map, stream=main)
+                src, count, stride = self.union, self.union_count, cfg.q * k
+            else:
+                src, count, stride = sel, None, k
+            loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
+            if g == 0:
+                ctx.append_resolve_rows_deferred(n, None, self.rows_dev[s], self.append_status,
+                                                 self.append_pos, src, count, stride, loc, fills,
+                                                 fc, -1, self.status[g], self.stats, stream=main)
+            else:
+                ctx.resolve_rows(n, None, src, count, stride, loc, fills, fc, -1, self.status[g],
+                                 self.stats, stream=main)
+            resolved = self._event()
+            resolved.record(main)
+            side.wait_event(resolved)
+            outs = self.outs[g] if distinct else self.outs[g][:1]
+            if g == 0:
+                ctx.fused_gather_append_rows(layers, n, None, loc, src, count, stride, outs,
+                                             self.rows_dev[s], self.append_pos,
+                                             self.gather_status, stream=side)
+            else:
+                ctx.fused_gather_rows(layers, n, None, loc, src, count, stride, outs,
+                                      self.gather_status, stream=side)
+            done = self._event()
+            done.record(side)
+            self._gather_done[(b, g)] = done
+            self._side_last = done
+            if not distinct:
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=main)
 
     # ------------------------------------------------------------------ residency
     def reclaim_pages(self, plan, stream=None):
@@ -324,11 +434,13 @@ class GpuRun:
 
     def snapshot(self) -> dict:
         """Device copies of the mutable state (metadata, hot caches, tails)."""
+        self.finish()
         return {"L": self.L.clone(), "tag": self.tag.clone(), "stamp": self.stamp.clone(),
                 "clock": self.clock.clone(), "hot": [h.clone() for h in self.hot],
                 "tail": [t.clone() for t in self.tail], "stats": self.stats.clone()}
 
     def restore(self, snap: dict) -> None:
+        self.finish()
         for name in ("L", "tag", "stamp", "clock", "stats"):
             getattr(self, name).copy_(snap[name])
         for dst, src in zip(self.hot, snap["hot"]):
@@ -336,7 +448,7 @@ class GpuRun:
         for dst, src in zip(self.tail, snap["tail"]):
             dst.copy_(src)
 
-    def capture(self, steps, prefetch_groups=0, fused: bool = False):
+    def capture(self, steps, prefetch_groups=0, fused: bool = False, pipelined: bool = False):
         """Capture the launches of `steps` into one HIP graph (nothing runs
         until it is replayed).  Each replay runs those decode steps again from
         whatever state the buffers hold."""
@@ -352,19 +464,33 @@ class GpuRun:
                                       "source with several resolving layers is disabled")
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()  # default priority
+        self.finish()
         cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for s in steps:
-                    self.step(s, prefetch_groups=prefetch_groups, fused=fused)
+        # no wait inside the capture on an event recorded before it
+        self._gather_done, self._side_last = {}, None
+        self._capturing = True
+        try:
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    for s in steps:
+                        self.step(s, prefetch_groups=prefetch_groups, fused=fused,
+                                  pipelined=pipelined)
+                    self.finish(cap)  # the side stream joins before the capture ends
+        finally:
+            self._capturing = False
+            self._events = []
+            self._gather_done, self._side_last = {}, None
         torch.cuda.current_stream().wait_stream(cap)
         return graph
 
     def _side(self, k: int = 1):
-        streams = self.__dict__.setdefault("_side_streams", {})
-        if k not in streams:
-            streams[k] = self.torch.cuda.Stream()  # default priority
-        return streams[k]
+        return self._side_streams[k]
+
+    def _event(self):
+        """A new event, kept referenced until the step or capture ends."""
+        ev = self.torch.cuda.Event()
+        self._events.append(ev)
+        return ev
 
     # ------------------------------------------------------------------ read-back (syncs)
     def state(self) -> dict:

@@ -214,8 +214,32 @@ int kvr_append_resolve_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, con
                             int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
                             int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream);
 
+/* kvr_append_resolve_rows with the tail write of the append deferred, so
+ * that the resolve of the next decode step may run while the previous step's
+ * rows are still being gathered (the step's KV write, "Memory split": the
+ * tail is the writable part; "Limits": decoded rows get a host copy).  The
+ * launch writes each appended row's host copy and advances L, but leaves its
+ * tail slot (L mod T) alone: that slot still holds the row L - T, which a
+ * gather of the previous step may be reading.  append_pos (device) int32 [n]
+ * receives, per entry, the position appended, or -1 when the entry appended
+ * nothing (a failed append or a bad request id).  The resolve itself sees
+ * the new length, exactly as after kvr_append_resolve_rows.  The appends are
+ * completed by kvr_fused_gather_append_rows with the same entries, new_rows
+ * and append_pos; until then a gather other than that one must not read the
+ * tail slot of an appended row.  Other arguments and errors as for
+ * kvr_append_resolve_rows. */
+int kvr_append_resolve_rows_deferred(kvr_ctx *ctx, int32_t n, const int32_t *req_ids,
+                                     const void *new_rows, int32_t *append_status,
+                                     int32_t *append_pos, const int32_t *sel,
+                                     const int32_t *sel_count, int32_t stride, uint32_t *loc,
+                                     kvr_fill *fills, int32_t *fill_count, int32_t fill_layer,
+                                     int32_t *status, kvr_stats *stats, void *stream);
+
 /* Gather resolved rows into contiguous per-request buffers, for several
- * payload layers sharing one location vector:
+ * payload layers sharing one location vector ("Adaptive DHiSparse", section
+ * "How it works", paragraph "Model-specific reuse": a layer reads its rows
+ * where the location vector says; layers with shared sparse indices but
+ * their own payloads each read their own bytes at the same locations):
  *   out[l] (device) [n][stride][R] for layers[l]; row j < cnt of request i is
  *   the R bytes at loc[i][j] in that layer (a fresh hot-cache row is read
  *   from its slot, so its fill must have run).  Invalid locations leave the
@@ -259,6 +283,22 @@ int kvr_fused_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers,
                           const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
                           const int32_t *count, int32_t stride, void *const *out, int32_t *status,
                           void *stream);
+
+/* kvr_fused_gather_rows that also completes the appends a
+ * kvr_append_resolve_rows_deferred call left pending for the same entries
+ * (same req_ids and n): for each entry with append_pos[i] >= 0, new_rows
+ * (device) [n_layers of the context][n][R] row i of every layer goes into
+ * tail slot append_pos[i] mod T, and a tail word of that entry naming that
+ * slot is gathered from new_rows (the same bytes).  The call must name every
+ * payload layer of the context exactly once (KVR_E_ARG otherwise), so every
+ * layer's tail receives its row; with an empty selection (stride 0 or
+ * counts 0) it still writes the rows.  Outputs and errors as for
+ * kvr_fused_gather_rows. */
+int kvr_fused_gather_append_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                                 const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                                 const int32_t *count, int32_t stride, void *const *out,
+                                 int32_t *status, const void *new_rows, const int32_t *append_pos,
+                                 void *stream);
 
 /* Verification block dedup ("Speculative state": queries share missing-row
  * retrieval).  Per request: union_rows[i][0..u) = the distinct rows of the q

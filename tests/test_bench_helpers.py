@@ -15,10 +15,13 @@ def test_recorded_traffic_matches_workload_schedule_and_source():
     assert records, "no counter summaries under profiles/"
     for fields in records:
         wl, sched = fields["workload"], fields["schedule"]
+        kernel = fields.get("kernel", "gather_kernel")
         if fields["source_sha256"] == bench.gather_source_hash():
-            assert bench.recorded_traffic(wl, sched) == int(fields["traffic_bytes_per_launch"])
+            assert bench.recorded_traffic(wl, sched, kernel) == int(
+                fields["traffic_bytes_per_launch"])
         else:  # the gather source changed since the counters were taken
-            assert bench.recorded_traffic(wl, sched) is None
+            assert bench.recorded_traffic(wl, sched, kernel) is None
+        assert bench.recorded_traffic(wl, sched, "no_such_kernel") is None
     assert bench.recorded_traffic("c2_glm_shared_indices", "no_such_schedule") is None
     assert bench.recorded_traffic("no_such_workload", "fused") is None
 
@@ -45,3 +48,15 @@ def test_layer_groups_reject_bad_sizes():
 
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_cpu_baseline_on_a_request_sample():
+    """The CPU baseline runs the oracle on the first n requests only, and
+    says so."""
+    from synth import tiny
+    cfg = tiny(5)
+    out = bench.cpu_baseline(cfg, 2, budget_s=2.0, min_s=0.05, n_reqs=2)
+    assert out["kind"] == "oracle" and out["unit"] == "rows/s" and out["value"] > 0
+    assert "requests 0..1 of 4" in out["sample"] and out["cores"] <= 2
+    full = bench.cpu_baseline(cfg, 2, budget_s=2.0, min_s=0.05)
+    assert f"all {cfg.n_req} requests" in full["sample"]

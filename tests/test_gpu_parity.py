@@ -24,7 +24,11 @@ def _gpu_run(inputs, **kw):
 
 
 def _compare_group(cfg, g_rec, o_rec, reqs, check_out=True):
-    """g_rec: GPU group record (all requests); o_rec: oracle record (reqs only)."""
+    """g_rec: GPU group record (all requests, or only `reqs` in that order
+    when g_rec["local"] is set); o_rec: oracle record (reqs only)."""
+    if g_rec.get("local"):
+        g_rec = dict(g_rec, local=False)
+        reqs = list(range(len(reqs)))
     idx = np.asarray(reqs)
     assert np.array_equal(g_rec["status"][idx], o_rec["status"])
     assert np.array_equal(g_rec["fill_count"][idx], o_rec["fill_count"])
@@ -51,6 +55,24 @@ def _compare_group(cfg, g_rec, o_rec, reqs, check_out=True):
                     f"gathered bytes, layer {l}, req {r}"
 
 
+def _group_sampled(gpu, g, reqs):
+    """The GPU's group record for `reqs` only (read back on the device side
+    first, so a full-size run copies little), marked local."""
+    import torch
+    gpu.torch.cuda.synchronize()
+    idx = torch.tensor(reqs, dtype=torch.long, device=gpu.dev)
+
+    def take(t):
+        return t.index_select(0, idx).cpu().numpy()
+
+    rec = {"local": True, "loc": take(gpu.loc[g]).view(np.uint32), "fills": take(gpu.fills[g]),
+           "fill_count": take(gpu.fill_count[g]), "status": take(gpu.status[g]),
+           "out": [take(o) for o in gpu.outs[g]]}
+    if gpu.cfg.q > 1:
+        rec.update(union=take(gpu.union), union_count=take(gpu.union_count), map=take(gpu.map))
+    return rec
+
+
 def _compare_state(gpu, run, reqs):
     st = gpu.state()
     idx = np.asarray(reqs)
@@ -62,7 +84,7 @@ def _compare_state(gpu, run, reqs):
 
 
 def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0, fused=False,
-                fuse_append=True):
+                fuse_append=True, pipelined=False):
     inputs = Inputs(cfg, max_new=max_new)
     reqs = list(range(cfg.n_req)) if reqs is None else list(reqs)
     pool = []
@@ -80,7 +102,7 @@ def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0,
             o = run.step(s, sels=[x[reqs] for x in sels])
             # groups of one step share buffers per group, so run the GPU step and
             # read every group back afterwards
-            gpu.step(s, prefetch_groups=prefetch_groups, fused=fused)
+            gpu.step(s, prefetch_groups=prefetch_groups, fused=fused, pipelined=pipelined)
             st = gpu.state()
             assert (st["L"] == inputs.length_at(s)).all()
             assert (gpu.append_status.cpu().numpy() == 0).all()
@@ -182,6 +204,158 @@ def test_fused_repeated_rows():
         gpu.close()
 
 
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_pipelined_schedule_parity(c):
+    """The pipelined schedule (resolves on the current stream, fused launches
+    on a side stream, the append's tail write deferred to the step's first
+    fused launch): the oracle's results at every step."""
+    _run_parity(tiny(c), fused=True, pipelined=True)
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_pipelined_schedule_back_to_back(c):
+    """All steps of the pipelined schedule issued with no host wait between
+    them, so each step's resolve runs beside the previous step's gathers;
+    after the last step its outputs, the metadata, the tails and the hot
+    payload equal the oracle's."""
+    import torch
+    cfg = tiny(c).with_(steps=8)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    try:
+        gpu.stage(range(cfg.steps))
+        for s in range(cfg.steps):
+            gpu.step(s, fused=True, pipelined=True)
+            o = run.step(s)
+        gpu.finish()
+        torch.cuda.synchronize()
+        for g in range(cfg.groups):
+            _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
+        _compare_state(gpu, run, reqs)
+        assert (gpu.gather_status.cpu().numpy() == 0).all()
+        for l in range(cfg.payload_layers):
+            assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l])
+            assert np.array_equal(gpu.tail[l].cpu().numpy(), run.src.tail[l])
+            lo, hi = cfg.H, cfg.H + cfg.steps
+            assert np.array_equal(gpu.host[l][:, lo:hi], run.src.host[l][:, lo:hi])
+    finally:
+        gpu.close()
+
+
+def test_pipelined_edges():
+    """The pipelined schedule without a tail, with one-row pages, with tight
+    budgets (failed requests) and with selections that name the newest row
+    (the one whose tail write is deferred) in every step."""
+    _run_parity(tiny(2).with_(T=0, steps=4), fused=True, pipelined=True)
+    _run_parity(tiny(4).with_(P=1, steps=4), fused=True, pipelined=True)
+    _run_parity(tiny(3).with_(B=160), fused=True, pipelined=True)
+    cfg = tiny(2).with_(steps=5)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    try:
+        for s in range(cfg.steps):
+            sel = inputs.selections(s, 0).copy()
+            newest = inputs.length_at(s) - 1
+            sel[:, 0, 3] = newest
+            sel[:, 0, 4] = newest - 1
+            sels = [sel]
+            gpu.stage([s], sels={s: sels})
+            o = run.step(s, sels=sels)
+            gpu.step(s, fused=True, pipelined=True)
+            _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
+            _compare_state(gpu, run, reqs)
+        for l in range(cfg.payload_layers):
+            assert np.array_equal(gpu.tail[l].cpu().numpy(), run.src.tail[l])
+    finally:
+        gpu.close()
+
+
+def test_deferred_append_entry_points_equal_plain_ones():
+    """kvr_append_resolve_rows_deferred + kvr_fused_gather_append_rows against
+    kvr_append_resolve_rows + kvr_fused_gather_rows on two copies of one
+    state: a permuted request list, a request already at capacity (its append
+    fails: position -1, nothing written), selections naming the newest row
+    and the row its tail slot held before, and an empty selection (the tail
+    rows are still written)."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2).with_(steps=3)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    runs = [_gpu_run(inputs), _gpu_run(inputs)]
+    try:
+        for g in runs:
+            g.stage(range(cfg.steps))
+            g.L[1] = inputs.host_rows
+        n, k = cfg.n_req, cfg.k
+        perm = [2, 0, 1]
+        req = torch.tensor(perm, dtype=torch.int32, device="cuda")
+        layers = list(range(cfg.payload_layers))
+        for s in range(cfg.steps):
+            sel = runs[0].sel_dev[s][0][perm].reshape(n, k).contiguous()
+            L = inputs.length_at(s)
+            sel[0, 0] = L - 1                      # the newest row (request 2)
+            sel[0, 1] = L - 1 - cfg.T              # the row its slot held
+            count = torch.full((n,), k if s != 1 else 0, dtype=torch.int32, device="cuda")
+            outs_all = []
+            for which, g in enumerate(runs):
+                ast = torch.full((n,), 99, dtype=torch.int32, device="cuda")
+                apos = torch.full((n,), 77, dtype=torch.int32, device="cuda")
+                loc = torch.zeros((n, k), dtype=torch.int32, device="cuda")
+                fills = torch.zeros((n, cfg.B, 2), dtype=torch.int32, device="cuda")
+                fc = torch.zeros(n, dtype=torch.int32, device="cuda")
+                st = torch.zeros(n, dtype=torch.int32, device="cuda")
+                gst = torch.zeros(n, dtype=torch.int32, device="cuda")
+                outs = [torch.full((n, k, cfg.R), 0xEE, dtype=torch.uint8, device="cuda")
+                        for _ in layers]
+                if which == 0:
+                    g.ctx.append_resolve_rows(n, req, g.rows_dev[s], ast, sel, count, k, loc,
+                                              fills, fc, -1, st, g.stats)
+                    g.ctx.fused_gather_rows(layers, n, req, loc, sel, count, k, outs, gst)
+                else:
+                    g.ctx.append_resolve_rows_deferred(n, req, g.rows_dev[s], ast, apos, sel,
+                                                       count, k, loc, fills, fc, -1, st, g.stats)
+                    # a layer list that misses or repeats a layer is refused
+                    with pytest.raises(kvr.KvrError):
+                        g.ctx.fused_gather_append_rows(layers[:-1], n, req, loc, sel, count, k,
+                                                       outs[:-1], g.rows_dev[s], apos, gst)
+                    with pytest.raises(kvr.KvrError):
+                        g.ctx.fused_gather_append_rows([0] * len(layers), n, req, loc, sel,
+                                                       count, k, outs, g.rows_dev[s], apos, gst)
+                    g.ctx.fused_gather_append_rows(layers[::-1], n, req, loc, sel, count, k,
+                                                   outs[::-1], g.rows_dev[s], apos, gst)
+                    torch.cuda.synchronize()
+                    assert apos.cpu().numpy().tolist() == [L - 1, L - 1, -1]
+                torch.cuda.synchronize()
+                outs_all.append(dict(ast=ast.cpu().numpy(), loc=loc.cpu().numpy(),
+                                     fills=fills.cpu().numpy(), fc=fc.cpu().numpy(),
+                                     st=st.cpu().numpy(), gst=gst.cpu().numpy(), state=g.state(),
+                                     out=[o.cpu().numpy() for o in outs],
+                                     tail=[t.cpu().numpy() for t in g.tail],
+                                     hot=[h.cpu().numpy() for h in g.hot],
+                                     host=[h.copy() for h in g.host], stats=g.stats_dict()))
+            a, b = outs_all
+            assert a["ast"].tolist() == b["ast"].tolist() == [0, 0, orc.E_CAPACITY]
+            for key in ("loc", "fc", "st", "gst"):
+                assert np.array_equal(a[key], b[key]), key
+            for i in range(n):
+                assert np.array_equal(a["fills"][i, :a["fc"][i]], b["fills"][i, :b["fc"][i]])
+            for key in ("L", "tag", "stamp", "clock"):
+                assert np.array_equal(a["state"][key], b["state"][key]), key
+            for l in layers:
+                assert np.array_equal(a["out"][l], b["out"][l]), l
+                assert np.array_equal(a["tail"][l], b["tail"][l]), l
+                assert np.array_equal(a["hot"][l], b["hot"][l]), l
+                assert np.array_equal(a["host"][l], b["host"][l]), l
+            assert a["stats"] == b["stats"]
+    finally:
+        for g in runs:
+            g.close()
+
+
 @pytest.mark.parametrize("c,B", [(2, 80), (2, 512), (3, 160), (3, 1024), (5, 120), (5, 2048)])
 def test_hot_budget_parity(c, B):
     """Hot-cache budgets below and above the reduced shapes' own: a tight
@@ -261,6 +435,155 @@ def test_edge_shapes_parity():
                dict(R=16, name="row16"), dict(R=4096, n_req=2, name="row4096"),
                dict(ready_frac=1.0, name="all_ready"), dict(ready_frac=0.0, name="none_ready")):
         _run_parity(base.with_(**kw))
+
+
+# ------------------------------------------------------------------ wide stamp spans
+
+
+def _wide_lru_state(inputs, seed, clock, empty_frac, hit_frac, bands):
+    """A valid hot-cache state far from what a short run reaches: per request
+    a share of empty slots (tag -1, stamp 0), a share of the first call's
+    pending rows already held (hits), other rows elsewhere, unique tags below
+    H, and stamps drawn from the given (lo, hi, weight) bands, all at most
+    `clock`.  Returns tags, stamps, clocks."""
+    cfg = inputs.cfg
+    rng = np.random.default_rng(seed)
+    n, B, H, P, T = cfg.n_req, cfg.B, cfg.H, cfg.P, cfg.T
+    L = inputs.length_at(0)
+    sel = inputs.selections(0, 0)[:, 0, :]
+    tags = np.full((n, B), -1, np.int32)
+    stamps = np.zeros((n, B), np.uint32)
+    weights = np.array([w for _, _, w in bands], float)
+    weights /= weights.sum()
+    for r in range(n):
+        pos = sel[r]
+        full = pos < (H // P) * P
+        ready = np.zeros(len(pos), bool)
+        ready[full] = inputs.page_map[r][pos[full] // P] >= 0
+        pend = np.unique(pos[(pos < max(0, L - T)) & ~ready])
+        n_hit = int(hit_frac * len(pend))
+        held = np.concatenate([rng.choice(pend, n_hit, replace=False),
+                               rng.choice(np.setdiff1d(np.arange(H), pend),
+                                          B - int(empty_frac * B) - n_hit, replace=False)])
+        slots = rng.permutation(B)[:len(held)]
+        tags[r, slots] = held
+        band = rng.choice(len(bands), len(held), p=weights)
+        lo = np.array([bands[b][0] for b in band], np.int64)
+        hi = np.array([bands[b][1] for b in band], np.int64)
+        stamps[r, slots] = (lo + (rng.random(len(held)) * (hi - lo + 1)).astype(np.int64)).astype(
+            np.uint32)
+    assert stamps.max() <= clock
+    return tags, stamps, np.full(n, clock, np.uint32)
+
+
+def _victim_shape(inputs, tags, stamps):
+    """Per request, for the first call of step 0: the stamp span over all
+    slots, the number of victims older than the threshold stamp (the m-th
+    smallest (stamp, slot) among the slots not hit) and their stamp spread:
+    the quantities that choose the resolve kernel's victim-selection branch."""
+    cfg = inputs.cfg
+    L = inputs.length_at(0)
+    sel = inputs.selections(0, 0)[:, 0, :]
+    out = []
+    for r in range(cfg.n_req):
+        pos = sel[r]
+        full = pos < (cfg.H // cfg.P) * cfg.P
+        ready = np.zeros(len(pos), bool)
+        ready[full] = inputs.page_map[r][pos[full] // cfg.P] >= 0
+        pend = np.unique(pos[(pos < max(0, L - cfg.T)) & ~ready]).tolist()
+        where = {int(t): b for b, t in enumerate(tags[r]) if t >= 0}
+        hit = {where[u] for u in pend if u in where}
+        cand = sorted((int(stamps[r, b]), b) for b in range(cfg.B) if b not in hit)
+        victims = cand[:len(pend) - len(hit)]
+        tau = victims[-1][0]
+        older = [st for st, _ in victims if st < tau]
+        out.append(dict(span=int(stamps[r].max()) - int(stamps[r].min()), older=len(older),
+                        spread=(max(older) - min(older)) if older else 0))
+    return out
+
+
+# name: (workload, clock, empty share, hit share of the pending rows, stamp
+# bands) and the branch it must reach: the stamp span picks one ballot-count
+# pass (< 64), one LDS-histogram pass (< 256) or 2/3/4 radix passes; the
+# victims older than the threshold are ranked by counting (<= 256), by the
+# 31-bit merge sort (spread < 2^18) or by the LDS bitonic network.
+_WIDE_CASES = {
+    "histogram_pass_merge_sort": (2, 100, 0.10, 0.15, [(1, 100, 1)]),
+    "two_passes_counting_ranks": (2, 5000, 0.0, 0.9, [(1, 5000, 1)]),
+    "ties_at_the_threshold": (2, 140, 0.05, 0.15, [(70, 70, 1), (140, 140, 1)]),
+    "bitonic_fallback_4096_slots": (2, 1_000_000, 0.0, 0.15,
+                                    [(1, 1000, 0.1), (300_000, 1_000_000, 0.9)]),
+    "two_passes_merge_sort_8192_slots": (5, 5000, 0.02, 0.15, [(1, 5000, 1)]),
+    "three_passes_bitonic_8192_slots": (5, 1_000_000, 0.0, 0.15,
+                                        [(1, 1000, 0.03), (300_000, 1_000_000, 0.97)]),
+    "four_passes_8192_slots": (5, 3_000_000_000, 0.05, 0.15, [(1, 3_000_000_000, 1)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_WIDE_CASES))
+def test_victim_selection_wide_stamp_spans(name):
+    """Hot-cache states with stamp spans from 100 to 3e9 ticks written into
+    both the GPU's and the oracle's metadata, then three decode steps of the
+    GLM-style (4096 slots) or long-context (8192 slots, four resolving layers)
+    shape: locations, fills, tags, stamps, clock and hot payload equal the
+    oracle's after every step.  Each case is checked to reach the victim
+    branch it names."""
+    import torch
+    c, clock, empty_frac, hit_frac, bands = _WIDE_CASES[name]
+    cfg = FULL[c].with_(n_req=2, steps=3)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    tags, stamps, clocks = _wide_lru_state(inputs, 17, clock, empty_frac, hit_frac, bands)
+    shape = _victim_shape(inputs, tags, stamps)
+    print(f"[wide] {name}: {shape}", flush=True)
+    for v in shape:
+        if "histogram" in name or "ties" in name:
+            assert 64 <= v["span"] < 256
+        elif "two_passes" in name:
+            assert 256 <= v["span"] < 1 << 16
+        elif "three_passes" in name:
+            assert 1 << 16 <= v["span"] < 1 << 24
+        elif "four_passes" in name:
+            assert v["span"] >= 1 << 24
+        if "counting_ranks" in name:
+            assert 1 < v["older"] <= 256 and v["spread"] > 0
+        elif "merge_sort" in name:
+            assert v["older"] > 256 and 0 < v["spread"] < 1 << 18
+        elif "bitonic" in name or "four_passes" in name:
+            assert v["older"] > 256 and v["spread"] >= 1 << 18
+        elif "ties" in name:
+            assert v["spread"] == 0
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    reqs = list(range(cfg.n_req))
+    try:
+        gpu.tag.copy_(torch.from_numpy(tags))
+        gpu.stamp.copy_(torch.from_numpy(stamps.view(np.int32)))
+        gpu.clock.copy_(torch.from_numpy(clocks.view(np.int32)))
+        run.src.tag[:] = tags
+        run.src.stamp[:] = stamps
+        run.src.clock[:] = clocks
+        assert (run.src.check() == 0).all()
+        for s in range(cfg.steps):
+            gpu.stage([s])
+            o = run.step(s)
+            gpu.step(s)
+            for g in range(cfg.groups):
+                rec = o["groups"][g]
+                assert (rec["status"] == 0).all()
+                _compare_group(cfg, gpu.group(g), rec, reqs)
+            _compare_state(gpu, run, reqs)
+        assert (run.src.check() == 0).all()
+        assert np.array_equal(gpu.hot[0].cpu().numpy(), run.src.hot[0])
+        print(f"[wide] {name}: ok", flush=True)
+    finally:
+        gpu.close()
+
+
+@pytest.mark.parametrize("c,kw", [(2, dict(B=1000, steps=80)), (5, dict(B=2000, steps=30))])
+def test_many_calls_parity(c, kw):
+    """More than 64 resolve calls per request with slots left empty (stamp 0),
+    so the stamp span outgrows the one-pass ballot count as a run ages."""
+    _run_parity(tiny(c).with_(**kw))
 
 
 # ------------------------------------------------------------------ kernels alone
@@ -740,11 +1063,12 @@ _CAPTURE_CRASH = ("capturing the fused schedule for one physical source (in an e
                   "until a cause is shown")
 
 
-@pytest.mark.parametrize("shape,prefetch_groups,fused", [
-    (2, 0, False), (2, 2, False), (5, 2, False), (4, 2, False), (2, 0, True),
-    pytest.param(5, 0, True, marks=pytest.mark.skip(reason=_CAPTURE_CRASH)),
-    (4, 0, True)])
-def test_graph_replays_match_oracle(shape, prefetch_groups, fused):
+@pytest.mark.parametrize("shape,prefetch_groups,fused,pipelined", [
+    (2, 0, False, False), (2, 2, False, False), (5, 2, False, False), (4, 2, False, False),
+    (2, 0, True, False),
+    pytest.param(5, 0, True, False, marks=pytest.mark.skip(reason=_CAPTURE_CRASH)),
+    (4, 0, True, False), (1, 0, True, True), (2, 0, True, True), (4, 0, True, True)])
+def test_graph_replays_match_oracle(shape, prefetch_groups, fused, pipelined):
     """Decode steps captured into HIP graphs give the oracle's results: a
     multi-step graph replayed once, then a one-step graph replayed three times
     (each replay is another decode step on the evolving state), with eager
@@ -762,16 +1086,17 @@ def test_graph_replays_match_oracle(shape, prefetch_groups, fused):
         _compare_state(gpu, run, reqs)
 
     try:
+        kw = dict(prefetch_groups=prefetch_groups, fused=fused, pipelined=pipelined)
         gpu.stage(range(cfg.steps))
-        gpu.step(0, prefetch_groups=prefetch_groups, fused=fused)
+        gpu.step(0, **kw)
         compare(run.step(0))
-        g = gpu.capture(range(1, 4), prefetch_groups=prefetch_groups, fused=fused)
+        g = gpu.capture(range(1, 4), **kw)
         g.replay()
         torch.cuda.synchronize()
         for s in range(1, 4):
             o = run.step(s)
         compare(o)
-        one = gpu.capture([4], prefetch_groups=prefetch_groups, fused=fused)
+        one = gpu.capture([4], **kw)
         for rep in range(3):
             one.replay()
             torch.cuda.synchronize()
@@ -793,21 +1118,24 @@ def test_bench_configuration_parity(c):
     import torch
     import bench
     cfg = FULL[c].with_(steps=32)
-    fused = bench.auto_fused(cfg)
+    schedule = bench.auto_schedule(cfg)
+    fused, pipelined = schedule in ("fused", "pipelined"), schedule == "pipelined"
     assert not (fused and cfg.reuse != "distinct")  # captured, as bench.py does
     warm, pg = 4, 2
     inputs = Inputs(cfg, max_new=cfg.steps)
-    print(f"[bench-config] {cfg.name}: fused={fused}", flush=True)
+    print(f"[bench-config] {cfg.name}: {schedule}", flush=True)
     gpu = _gpu_run(inputs)
     run = OracleRun(inputs)
     reqs = list(range(cfg.n_req))
     try:
         gpu.stage(range(cfg.steps))
         for s in range(warm):
-            gpu.step(s, prefetch_groups=pg, fused=fused)
+            gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+        gpu.finish()
         torch.cuda.synchronize()
         snap = gpu.snapshot()
-        graph = gpu.capture(range(warm, cfg.steps), prefetch_groups=pg, fused=fused)
+        graph = gpu.capture(range(warm, cfg.steps), prefetch_groups=pg, fused=fused,
+                            pipelined=pipelined)
         torch.cuda.synchronize()
         for s in range(cfg.steps):
             o = run.step(s)
@@ -824,6 +1152,68 @@ def test_bench_configuration_parity(c):
             for l in range(cfg.payload_layers):
                 assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l]), f"hot {l}"
         print(f"[bench-config] {cfg.name}: ok", flush=True)
+    finally:
+        gpu.close()
+
+
+def test_bench_configuration_parity_long_context():
+    """The long-context configuration bench.py times, at full size (64
+    requests of 524288 rows, 4 resolving layers per step): its default
+    schedule (fused, issued eagerly since its graph capture is off), 4
+    warm-up steps, then the 28 timed steps.  On requests 0, 1, 42 and 63 (the
+    oracle follows them exactly; requests never interact): first step by step
+    with the locations, fills, gathered bytes, metadata and hot payload
+    compared after every step; then again from the same snapshot with the 28
+    steps issued back to back as when timed, compared after the last."""
+    import torch
+    import bench
+    cfg = FULL[5].with_(steps=32)
+    schedule = bench.auto_schedule(cfg)
+    fused, pipelined = schedule in ("fused", "pipelined"), schedule == "pipelined"
+    assert fused and cfg.reuse != "distinct"
+    warm = 4
+    reqs = [0, 1, 42, 63]
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    pool = []
+    for l in range(cfg.payload_layers):
+        p = np.empty((cfg.pool_pages, cfg.P, cfg.R), dtype=np.uint8)
+        inputs.fill_pool(l, p)
+        pool.append(p)
+    print(f"[bench-config] {cfg.name}: {schedule} eager, reqs={reqs}", flush=True)
+    gpu = _gpu_run(inputs, pool_host=pool)
+    run = OracleRun(inputs, reqs=reqs, pool=pool)
+    idx = torch.tensor(reqs, dtype=torch.long, device="cuda")
+
+    def compare(o):
+        for g in range(cfg.groups):
+            _compare_group(cfg, _group_sampled(gpu, g, reqs), o["groups"][g], reqs)
+        _compare_state(gpu, run, reqs)
+        assert np.array_equal(gpu.hot[0].index_select(0, idx).cpu().numpy(), run.src.hot[0])
+        assert (gpu.gather_status.cpu().numpy() == 0).all()
+        assert (gpu.append_status.cpu().numpy() == 0).all()
+        for g in range(cfg.groups):
+            assert (gpu.status[g].cpu().numpy() == 0).all()
+
+    try:
+        gpu.stage(range(cfg.steps))
+        for s in range(warm):
+            gpu.step(s, fused=fused, pipelined=pipelined)
+            o = run.step(s)
+        torch.cuda.synchronize()
+        compare(o)
+        snap = gpu.snapshot()
+        for s in range(warm, cfg.steps):
+            gpu.step(s, fused=fused, pipelined=pipelined)
+            o = run.step(s)
+            compare(o)
+        print(f"[bench-config] {cfg.name}: step by step ok", flush=True)
+        gpu.restore(snap)
+        for s in range(warm, cfg.steps):
+            gpu.step(s, fused=fused, pipelined=pipelined)
+        gpu.finish()
+        torch.cuda.synchronize()
+        compare(o)
+        print(f"[bench-config] {cfg.name}: back to back ok", flush=True)
     finally:
         gpu.close()
 
