@@ -61,12 +61,16 @@ def parse():
                     help="layer groups whose host fills overlap earlier gathers: a count "
                          "(equal groups, 0 = off) or comma-separated group sizes")
     ap.add_argument("--schedule", default="auto",
-                    choices=["auto", "prefetch", "fused", "pipelined"],
+                    choices=["auto", "prefetch", "fused", "pipelined", "merged"],
                     help="fused: host fills and the gather of the rows they bring in as one "
                          "pass beside the gather of all other rows; pipelined: the fused "
                          "launches on a side stream so that each resolve (the next step's "
-                         "included) runs beside the previous gathers; prefetch: fills in layer "
-                         "groups ahead of per-group gathers; auto: see auto_schedule()")
+                         "included) runs beside the previous gathers; merged: the same overlap "
+                         "in one launch per resolve (gather of the previous resolve beside "
+                         "it) on one stream; prefetch: fills in layer groups ahead of "
+                         "per-group gathers; auto: see auto_schedule()")
+    ap.add_argument("--step-buffers", type=int, default=0,
+                    help="sets of per-step output buffers (0: the runner's default)")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of the K steps from the same state (median reported)")
     ap.add_argument("--hot-slots", type=int, default=0,
@@ -130,9 +134,19 @@ def auto_fused(cfg) -> bool:
 
 def auto_schedule(cfg) -> str:
     """The default schedule: where the fused schedule is the default
-    (auto_fused), its pipelined form, whose resolves leave the critical path;
-    else prefetch."""
-    return "pipelined" if auto_fused(cfg) else "prefetch"
+    (auto_fused), a form whose resolves leave the critical path: merged (one
+    launch per resolve, beside the previous gather) except for verify blocks,
+    whose large resident gather runs slower in the merged launch's
+    1024-thread workgroups, which take the pipelined form; else prefetch."""
+    if not auto_fused(cfg):
+        return "prefetch"
+    return "pipelined" if cfg.q > 1 else "merged"
+
+
+def schedule_kwargs(schedule: str) -> dict:
+    """GpuRun.step flags of a schedule name (prefetch groups aside)."""
+    return dict(fused=schedule in ("fused", "pipelined", "merged"),
+                pipelined=schedule == "pipelined", merged=schedule == "merged")
 
 
 def cpu_baseline(cfg, total_steps, budget_s, min_s=10.0, threads=None, n_reqs=None):
@@ -458,22 +472,22 @@ def main():
         cfg = cfg.with_(B=args.hot_slots)
     inputs = Inputs(cfg, max_new=total)
     log(f"workload {cfg.name}: staging {total} steps")
-    gpu = GpuRun(inputs)
+    gpu = GpuRun(inputs, step_buffers=args.step_buffers)
     gpu.stage(range(total))
     log("staged; warming up")
     counts = rows_per_group(inputs, range(W, total))
     pg = args.prefetch_groups
     pg = int(pg) if "," not in pg else tuple(int(x) for x in pg.split(","))
     schedule = auto_schedule(cfg) if args.schedule == "auto" else args.schedule
-    pipelined = schedule == "pipelined"
-    fused = schedule in ("fused", "pipelined")
+    kw = dict(prefetch_groups=pg, **schedule_kwargs(schedule))
+    fused, merged = kw["fused"], kw["merged"]
     no_graph = args.no_graph
     if fused and cfg.reuse != "distinct" and not no_graph:
         # its graph capture is disabled (GpuRun.capture): timed eagerly
         log("the fused schedule of one physical source runs eagerly (no graph)")
         no_graph = True
     for s in range(W):
-        gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+        gpu.step(s, **kw)
     gpu.finish()
     torch.cuda.synchronize()
     snap = gpu.snapshot()
@@ -496,15 +510,17 @@ def main():
         gpu.restore(snap)
         gpu.ctx.timing_begin(64 * K + 64)
         for s in range(W, total):
-            gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+            gpu.step(s, **kw)
         gpu.finish()
-        fused_runs = launch_means_ms(gpu.ctx.timing_end()).get("fused", [])
+        rec = launch_means_ms(gpu.ctx.timing_end())
         torch.cuda.synchronize()
-        launches["fused"] = fused_runs
+        launches["fused"] = rec.get("fused", [])
+        if merged:
+            # each launch but the last gathers one selection beside the next resolve
+            launches["step"] = rec.get("step", [])
     if not no_graph:
         gpu.restore(snap)
-        graph = gpu.capture(range(W, total), prefetch_groups=pg, fused=fused,
-                            pipelined=pipelined)
+        graph = gpu.capture(range(W, total), **kw)
         torch.cuda.synchronize()
         log("captured the timed steps into one graph")
 
@@ -544,7 +560,7 @@ def main():
         start.record()
         if no_graph:
             for s in range(W, total):
-                gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+                gpu.step(s, **kw)
             gpu.finish()
         else:
             graph.replay()
@@ -619,13 +635,15 @@ def main():
 
     # The roofline is that of the kernel that takes most of the timed pass.
     if fused:
-        f_list = launches.get("fused", [])
+        # the launches that gather: fused ones, and with the merged schedule
+        # the step launches (a gather beside the next resolve)
+        f_list = launches.get("step", []) + launches.get("fused", [])
         n_launch = max(1, len(f_list))
         d_ms = sum(f_list) / n_launch
         d_host = n_out * fresh * cfg.R / n_launch
         d_hbm = (n_out * entries * 2 * cfg.R + entries * 4 + fresh * 4) / n_launch
-        d_kernel = "fused_gather_kernel"
-        d_timing = ("start/end events of each fused dispatch in an eager pass of the timed "
+        d_kernel = "step_kernel" if merged else "fused_gather_kernel"
+        d_timing = ("start/end events of each gathering dispatch in an eager pass of the timed "
                     "pass's own launches (same streams and overlaps) over the same steps from "
                     "the same starting state")
     elif fill_calls and sum(fill_calls) >= sum(g_list):

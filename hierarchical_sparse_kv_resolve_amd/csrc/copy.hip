@@ -166,8 +166,12 @@ bool tile_magic_exact(int32_t row_bytes)
 {
     Shape sh{};
     sh.R = row_bytes;
-    for (int unroll : {kUnroll, kGatherUnroll}) {
-        const TileShape ts = tile_for(sh, unroll);
+    // the tiles of 256-thread workgroups (host and device unrolls) and of the
+    // 1024-thread workgroups that gather beside a resolve
+    const int shapes[3][2] = {{kUnroll, kRowThreads}, {kGatherUnroll, kRowThreads},
+                              {kGatherUnroll, 1024}};
+    for (const auto &u : shapes) {
+        const TileShape ts = tile_for(sh, u[0], u[1]);
         for (uint32_t c = 0; c < (uint32_t)(ts.rows * ts.chunks); ++c)
             if ((uint32_t)(((uint64_t)c * ts.magic) >> 32) != c / (uint32_t)ts.chunks)
                 return false;

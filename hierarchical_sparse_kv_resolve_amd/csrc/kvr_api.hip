@@ -212,6 +212,8 @@ int kvr_create(const kvr_config *cfg, kvr_ctx **out)
         e = kvr::prepare_resolve_kernel();
     if (e == hipSuccess)
         e = kvr::prepare_dedup_kernel();
+    if (e == hipSuccess)
+        e = kvr::prepare_step_kernel();
     if (e != hipSuccess) {
         kvr_destroy(ctx);
         return hip_fail(e, "kernel set-up");
@@ -315,11 +317,9 @@ int kvr_append_rows(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void 
     return e == hipSuccess ? ok() : hip_fail(e, "append launch");
 }
 
-static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
-                         int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
-                         int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
-                         int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream,
-                         int32_t *append_pos = nullptr)
+static int check_resolve(kvr_ctx *ctx, int32_t n, const void *new_rows, int32_t *append_status,
+                         const int32_t *sel, int32_t stride, uint32_t *loc, kvr_fill *fills,
+                         int32_t *fill_count, int32_t fill_layer, int32_t *status)
 {
     if (int rc = check_ctx(ctx))
         return rc;
@@ -339,6 +339,18 @@ static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const 
     if (fill_layer != -1)
         if (int rc = check_layer(ctx, fill_layer))
             return rc;
+    return KVR_OK;
+}
+
+static int resolve_entry(kvr_ctx *ctx, int32_t n, const int32_t *req_ids, const void *new_rows,
+                         int32_t *append_status, const int32_t *sel, const int32_t *sel_count,
+                         int32_t stride, uint32_t *loc, kvr_fill *fills, int32_t *fill_count,
+                         int32_t fill_layer, int32_t *status, kvr_stats *stats, void *stream,
+                         int32_t *append_pos = nullptr)
+{
+    if (int rc = check_resolve(ctx, n, new_rows, append_status, sel, stride, loc, fills,
+                               fill_count, fill_layer, status))
+        return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (int rc = check_stream(ctx, s))
         return rc;
@@ -391,11 +403,9 @@ int kvr_append_resolve_rows_deferred(kvr_ctx *ctx, int32_t n, const int32_t *req
                          fills, fill_count, fill_layer, status, stats, stream, append_pos);
 }
 
-static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
-                        int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
-                        const int32_t *count, int32_t stride, void *const *out, int32_t *status,
-                        void *stream, const void *new_rows = nullptr,
-                        const int32_t *append_pos = nullptr)
+static int check_gather(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
+                        const uint32_t *loc, int32_t stride, void *const *out,
+                        const void *new_rows, const int32_t *append_pos)
 {
     if (int rc = check_ctx(ctx, false))
         return rc;
@@ -413,8 +423,7 @@ static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
         if (!out[t] && n > 0 && stride > 0)
             return fail(KVR_E_ARG, "out[%d] is null", t);
     }
-    const bool deferred = append_pos != nullptr;
-    if (deferred) {
+    if (append_pos) {
         // the appended rows go to the tail of every payload layer: the call
         // must name each layer of the context once
         if (!ctx->meta_bound)
@@ -429,6 +438,18 @@ static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
                 if (layers[u] == layers[t])
                     return fail(KVR_E_ARG, "layer %d named twice", layers[t]);
     }
+    return KVR_OK;
+}
+
+static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
+                        int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                        const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                        void *stream, const void *new_rows = nullptr,
+                        const int32_t *append_pos = nullptr)
+{
+    if (int rc = check_gather(ctx, n_layers, layers, n, loc, stride, out, new_rows, append_pos))
+        return rc;
+    const bool deferred = append_pos != nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int rc = check_stream(ctx, s);
     // one launch per group of up to kGatherLayersPerLaunch layers (with
@@ -502,6 +523,66 @@ int kvr_fused_gather_append_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *
         return fail(KVR_E_ARG, "append_pos is required");
     return gather_entry(ctx, kvr::kGatherFused, n_layers, layers, n, req_ids, loc, sel, count,
                         stride, out, status, stream, new_rows, append_pos);
+}
+
+int kvr_gather_resolve_rows(kvr_ctx *ctx, const kvr_gather_call *g, const kvr_resolve_call *r,
+                            void *stream)
+{
+    if (!g && !r)
+        return fail(KVR_E_ARG, "a gather or a resolve call is required");
+    if (g && g->n > 0 && g->stride > 0 && g->n_layers > 0 && !g->sel)
+        return fail(KVR_E_ARG, "gather: sel is required");
+    if (g && g->n > 0 && !g->append_pos && g->new_rows)
+        return fail(KVR_E_ARG, "gather: new_rows without append_pos");
+    if (g) {
+        if (int rc = check_gather(ctx, g->n_layers, g->layers, g->n, g->loc, g->stride, g->out,
+                                  g->new_rows, g->append_pos))
+            return rc;
+    }
+    if (r) {
+        // an append beside a gather must leave the tail to a later gather
+        if (r->n > 0 && r->new_rows && !r->append_pos)
+            return fail(KVR_E_ARG, "resolve: an append needs append_pos (it is deferred)");
+        if (int rc = check_resolve(ctx, r->n, r->new_rows, r->append_status, r->sel, r->stride,
+                                   r->loc, r->fills, r->fill_count, -1, r->status))
+            return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    const bool has_g = g && g->n > 0 && g->n_layers > 0 && (g->stride > 0 || g->append_pos);
+    const bool has_r = r && r->n > 0;
+    if (!has_g && !has_r)
+        return ok();
+    hipError_t e = hipSuccess;
+    if (!has_g) {
+        e = kvr::launch_resolve(ctx, r->n, r->req_ids, r->sel, r->sel_count, r->stride, r->loc,
+                                r->fills, r->fill_count, r->status, r->stats, 0,
+                                static_cast<const uint8_t *>(r->new_rows), r->append_status,
+                                r->append_pos, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "resolve launch");
+    }
+    if (!has_r)
+        return gather_entry(ctx, kvr::kGatherFused, g->n_layers, g->layers, g->n, g->req_ids,
+                            g->loc, g->sel, g->count, g->stride, g->out, g->status, stream,
+                            g->new_rows, g->append_pos);
+    // the first (up to kGatherLayersPerLaunch) layers share the launch with
+    // the resolve; more layers are gathered by launches of their own after it
+    kvr::GatherTarget targets[kvr::kGatherLayersPerLaunch];
+    const int32_t nt0 = g->n_layers < kvr::kGatherLayersPerLaunch ? g->n_layers
+                                                                   : kvr::kGatherLayersPerLaunch;
+    for (int32_t t = 0; t < nt0; ++t) {
+        targets[t].layer = g->layers[t];
+        targets[t].out = static_cast<uint8_t *>(g->out[t]);
+    }
+    e = kvr::launch_step(ctx, *g, targets, nt0, *r, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "gather-resolve launch");
+    if (g->n_layers > nt0)
+        return gather_entry(ctx, kvr::kGatherFused, g->n_layers - nt0, g->layers + nt0, g->n,
+                            g->req_ids, g->loc, g->sel, g->count, g->stride, g->out + nt0,
+                            g->status, stream, g->new_rows, g->append_pos);
+    return ok();
 }
 
 int kvr_dedup_verify_selections(kvr_ctx *ctx, int32_t n, int32_t q, int32_t k, const int32_t *sel,

@@ -118,6 +118,9 @@ hipError_t launch_resolve(const kvr_ctx *c, int32_t n, const int32_t *req_ids, c
                           int32_t count_host_bytes, const uint8_t *new_rows,
                           int32_t *append_status, int32_t *append_pos, hipStream_t s);
 size_t resolve_lds_bytes(const Shape &sh);
+// The resolve workgroup's dynamic LDS: victim keys (vc entries), hash (hs
+// entries) and miss bitmap (bw words); 0 when the shape does not fit.
+size_t resolve_lds_layout(const Shape &sh, int32_t *vc, int32_t *hs, int32_t *bw);
 hipError_t prepare_resolve_kernel();
 
 // Copies the fills of each request from the host store into the hot cache of
@@ -143,6 +146,12 @@ hipError_t launch_gather(const kvr_ctx *c, int32_t mode, const GatherTarget *tar
                          const int32_t *sel, const int32_t *count, int32_t stride, int32_t *status,
                          hipStream_t s, const uint8_t *new_rows = nullptr,
                          const int32_t *append_pos = nullptr);
+
+// One launch: the fused gather g (its first nt layers, targets) beside the
+// resolve r (no host fill; an append must be deferred).
+hipError_t launch_step(const kvr_ctx *c, const kvr_gather_call &g, const GatherTarget *targets,
+                       int32_t nt, const kvr_resolve_call &r, hipStream_t s);
+hipError_t prepare_step_kernel();
 
 hipError_t launch_append(const kvr_ctx *c, int32_t n, const int32_t *req_ids,
                          const uint8_t *new_rows, int32_t *status, hipStream_t s);

@@ -42,13 +42,14 @@ __device__ __forceinline__ void store_chunk(uint8_t *p, const u32x4 &v)
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-// As many whole rows as `unroll` chunks per lane cover, and the multiplier
-// that divides a chunk index by the row's chunk count.
-inline TileShape tile_for(const Shape &sh, int unroll)
+// As many whole rows as `unroll` chunks per lane of a workgroup of `threads`
+// cover, and the multiplier that divides a chunk index by the row's chunk
+// count.
+inline TileShape tile_for(const Shape &sh, int unroll, int threads = kRowThreads)
 {
     TileShape ts;
     ts.chunks = sh.R / 16;
-    int rows = (kRowThreads * unroll) / ts.chunks;
+    int rows = (threads * unroll) / ts.chunks;
     ts.rows = rows < 1 ? 1 : (rows > kMaxTileRows ? kMaxTileRows : rows);
     ts.magic = (((uint64_t)1 << 32) + ts.chunks - 1) / ts.chunks;
     return ts;

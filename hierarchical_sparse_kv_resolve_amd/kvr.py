@@ -34,6 +34,7 @@ REUSE_DISTINCT_PAYLOAD = 1
 EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "kvr_bind_layer",
            "kvr_init_state", "kvr_append_rows", "kvr_resolve_rows", "kvr_append_resolve_rows",
            "kvr_append_resolve_rows_deferred", "kvr_gather_rows", "kvr_fused_gather_append_rows",
+           "kvr_gather_resolve_rows",
            "kvr_dedup_verify_selections", "kvr_reuse_locations", "kvr_status_summary",
            "kvr_host_alloc", "kvr_host_free", "kvr_timing_begin", "kvr_timing_end",
            "kvr_reclaim_pages", "kvr_restore_pages", "kvr_gather_resident_rows",
@@ -45,7 +46,7 @@ EXPORTS = ("kvr_create", "kvr_destroy", "kvr_last_error", "kvr_bind_metadata", "
            "kvr_staging_acquire", "kvr_staging_release")
 
 # kvr_kernel: kinds of the library's kernel launches (launch timing).
-KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state", "fused")
+KERNEL_NAMES = ("append", "resolve", "refill", "gather", "dedup", "state", "fused", "step")
 
 
 class KvrError(RuntimeError):
@@ -64,6 +65,26 @@ class Config(ctypes.Structure):
 
 
 STATS_FIELDS = ("calls", "tail", "page", "hit", "miss", "fill", "host_bytes", "error")
+
+
+class GatherCall(ctypes.Structure):
+    """kvr_gather_call of include/kvr.h."""
+    _fields_ = [("n_layers", ctypes.c_int32), ("layers", ctypes.c_void_p),
+                ("n", ctypes.c_int32), ("req_ids", ctypes.c_void_p), ("loc", ctypes.c_void_p),
+                ("sel", ctypes.c_void_p), ("count", ctypes.c_void_p), ("stride", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("new_rows", ctypes.c_void_p), ("append_pos", ctypes.c_void_p)]
+
+
+class ResolveCall(ctypes.Structure):
+    """kvr_resolve_call of include/kvr.h."""
+    _fields_ = [("n", ctypes.c_int32), ("req_ids", ctypes.c_void_p),
+                ("new_rows", ctypes.c_void_p), ("append_status", ctypes.c_void_p),
+                ("append_pos", ctypes.c_void_p), ("sel", ctypes.c_void_p),
+                ("sel_count", ctypes.c_void_p), ("stride", ctypes.c_int32),
+                ("loc", ctypes.c_void_p), ("fills", ctypes.c_void_p),
+                ("fill_count", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("stats", ctypes.c_void_p)]
 
 _lib = None
 
@@ -92,6 +113,7 @@ def lib():
             "kvr_fill_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
             "kvr_fused_gather_rows": [P, I, P, I, P, P, P, P, I, P, P, P],
             "kvr_fused_gather_append_rows": [P, I, P, I, P, P, P, P, I, P, P, P, P, P],
+            "kvr_gather_resolve_rows": [P, P, P, P],
             "kvr_dedup_verify_selections": [P, I, I, I, P, P, P, P, P],
             "kvr_reuse_locations": [P, I, I, P, I, P, P, P, P, I, P, P, P, P],
             "kvr_status_summary": [P, I, P],
@@ -360,6 +382,43 @@ class Context:
             self.handle, nl, arr_l, n, rid, lc, sl, cnt, stride, arr_o, st,
             _dev(new_rows, "new_rows", NL * n * R), _dev(append_pos, "append_pos", 4 * n),
             _stream(stream)))
+
+    def gather_resolve_rows(self, gather=None, resolve=None, stream=None):
+        """kvr_gather_resolve_rows.  gather: dict(layers, n, req_ids, loc, sel,
+        count, stride, outs, status, new_rows, append_pos) or None; resolve:
+        dict(n, req_ids, new_rows, append_status, append_pos, sel, sel_count,
+        stride, loc, fills, fill_count, status, stats) or None.  Missing keys
+        are NULL."""
+        keep = []
+        g_ptr = r_ptr = None
+        NL, R = self.cfg.n_layers, self.cfg.row_bytes
+        if gather is not None:
+            g = {**dict(req_ids=None, count=None, status=None, new_rows=None, append_pos=None,
+                        sel=None), **gather}
+            n, stride = g["n"], g["stride"]
+            nl, arr_l, rid, lc, cnt, arr_o, st = self._gather_args(
+                g["layers"], n, g["req_ids"], g["loc"], g["count"], stride, g["outs"], g["status"])
+            gc = GatherCall(nl, ctypes.addressof(arr_l), n, rid, lc,
+                            _dev(g["sel"], "sel", 4 * max(n, 0) * max(stride, 0)), cnt, stride,
+                            ctypes.addressof(arr_o), st,
+                            _dev(g["new_rows"], "new_rows", NL * n * R),
+                            _dev(g["append_pos"], "append_pos", 4 * n))
+            keep += [arr_l, arr_o, gc]
+            g_ptr = ctypes.addressof(gc)
+        if resolve is not None:
+            r = {**dict(req_ids=None, new_rows=None, append_status=None, append_pos=None,
+                        sel_count=None, stats=None), **resolve}
+            n = r["n"]
+            rid, sl, sc, lc, fl, fc, st, sts = self._resolve_args(
+                n, r["req_ids"], r["sel"], r["sel_count"], r["stride"], r["loc"], r["fills"],
+                r["fill_count"], r["status"], r["stats"])
+            rc = ResolveCall(n, rid, _dev(r["new_rows"], "new_rows", NL * n * R),
+                             _dev(r["append_status"], "append_status", 4 * n),
+                             _dev(r["append_pos"], "append_pos", 4 * n), sl, sc, r["stride"], lc,
+                             fl, fc, st, sts)
+            keep.append(rc)
+            r_ptr = ctypes.addressof(rc)
+        _check(lib().kvr_gather_resolve_rows(self.handle, g_ptr, r_ptr, _stream(stream)))
 
     def dedup_verify_selections(self, n, q, k, sel, union_rows, union_count, map_, stream=None):
         m = max(n, 0) * max(q, 0) * max(k, 0)

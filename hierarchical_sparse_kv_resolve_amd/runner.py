@@ -45,9 +45,13 @@ def layer_groups(n_layers: int, prefetch_groups) -> list:
 
 
 class GpuRun:
-    def __init__(self, inputs, pool_host=None, device: str = "cuda", fuse_append: bool = True):
+    def __init__(self, inputs, pool_host=None, device: str = "cuda", fuse_append: bool = True,
+                 step_buffers: int = 0):
         """fuse_append: the step's append runs inside its first resolve launch
-        (kvr_append_resolve_rows) instead of as a launch of its own."""
+        (kvr_append_resolve_rows) instead of as a launch of its own.
+        step_buffers: sets of per-step output buffers that alternate by step
+        (0: two when a step has one resolving layer, else one); more sets
+        let the pipelined schedule's resolves run further ahead."""
         import torch
         self.torch = torch
         self.fuse_append = fuse_append
@@ -100,7 +104,7 @@ class GpuRun:
         # still reads; with several resolving layers each layer's set is
         # rewritten only a whole step later.  The attributes below always
         # name the set of the step issued last.
-        self._nbuf = 2 if G == 1 else 1
+        self._nbuf = step_buffers if step_buffers > 0 else (2 if G == 1 else 1)
         self._sets = []
         for _ in range(self._nbuf):
             bs = {"loc": [torch.empty((n, cap), dtype=i32, device=dev) for _ in range(G)],
@@ -131,6 +135,8 @@ class GpuRun:
         # that read each (buffer set, group), and after the last side launch
         self._gather_done = {}
         self._side_last = None
+        # merged schedule: the gather of the last resolve, not yet issued
+        self._pending = None
 
     def _use_set(self, b: int):
         bs = self._sets[b]
@@ -141,10 +147,15 @@ class GpuRun:
             self.union, self.union_count, self.map = bs["union"], bs["union_count"], bs["map"]
 
     def finish(self, stream=None):
-        """Make `stream` (default: the current one) wait for the side-stream
-        work of the pipelined schedule issued so far.  No host wait."""
+        """Complete the steps issued so far on `stream` (default: the current
+        one): issue the merged schedule's last gather, and wait for the
+        pipelined schedule's side-stream work.  No host wait."""
+        st = stream or self.torch.cuda.current_stream()
+        if self._pending is not None:
+            self.ctx.gather_resolve_rows(gather=self._pending, resolve=None, stream=st)
+            self._pending = None
         if self._side_last is not None:
-            (stream or self.torch.cuda.current_stream()).wait_event(self._side_last)
+            st.wait_event(self._side_last)
 
     def close(self):
         self.torch.cuda.synchronize()
@@ -166,7 +177,7 @@ class GpuRun:
             self.rows_dev[s] = torch.from_numpy(self.inputs.new_rows(s)).to(self.dev)
 
     def step(self, s: int, prefetch_groups=0, serialize: bool = False, fused: bool = False,
-             pipelined: bool = False):
+             pipelined: bool = False, merged: bool = False):
         """Enqueue decode step s (staged beforehand) on the current stream.  No
         host synchronisation.
 
@@ -182,6 +193,12 @@ class GpuRun:
         Call finish() before work on the current stream that needs this
         step's gathered rows or hot payload (capture() and the read-back
         helpers do).
+
+        merged=True (with fused=True, not serialized): the same overlap on
+        one stream with no wait between queues: each resolve is issued in
+        one launch with the gather of the resolve before it
+        (gather_resolve_rows), and the step's last gather waits for the next
+        step's first resolve, or for finish().
 
         prefetch_groups = 0: resolve fills payload layer 0 from host, one
         replay call fills the other layers, one gather call covers them all.
@@ -215,11 +232,14 @@ class GpuRun:
             # schedule wait on stay referenced by _gather_done / _side_last)
             self._events = []
         self._use_set(s % self._nbuf)
-        if pipelined:
-            if not fused or serialize or not self.fuse_append:
-                raise ValueError("the pipelined schedule is the fused one, not serialized, "
-                                 "with the append inside the first resolve")
-            self._step_pipelined(s)
+        if pipelined or merged:
+            if not fused or serialize or not self.fuse_append or (pipelined and merged):
+                raise ValueError("the pipelined and merged schedules are the fused one, not "
+                                 "serialized, with the append inside the first resolve")
+            if merged:
+                self._step_merged(s)
+            else:
+                self._step_pipelined(s)
             return
         self.finish()  # other schedules start from a joined side stream
         main = torch.cuda.current_stream()
@@ -356,6 +376,39 @@ class GpuRun:
                                     [self.outs[g][l] for l in grp], self.gather_status,
                                     stream=main)
 
+    def _step_merged(self, s: int):
+        torch = self.torch
+        cfg, ctx, n = self.cfg, self.ctx, self.n
+        main = torch.cuda.current_stream()
+        distinct = cfg.reuse == "distinct"
+        layers = list(range(self.nl)) if distinct else [0]
+        for g in range(cfg.groups):
+            sel = self.sel_dev[s][g]
+            k = sel.shape[-1]
+            if cfg.q > 1:
+                ctx.dedup_verify_selections(n, cfg.q, k, sel, self.union, self.union_count,
+                                            self.map, stream=main)
+                src, count, stride = self.union, self.union_count, cfg.q * k
+            else:
+                src, count, stride = sel, None, k
+            loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
+            res = dict(n=n, sel=src, sel_count=count, stride=stride, loc=loc, fills=fills,
+                       fill_count=fc, status=self.status[g], stats=self.stats)
+            if g == 0:
+                res.update(new_rows=self.rows_dev[s], append_status=self.append_status,
+                           append_pos=self.append_pos)
+            ctx.gather_resolve_rows(gather=self._pending, resolve=res, stream=main)
+            gat = dict(layers=layers, n=n, loc=loc, sel=src, count=count, stride=stride,
+                       outs=self.outs[g] if distinct else self.outs[g][:1],
+                       status=self.gather_status)
+            if g == 0:
+                gat.update(new_rows=self.rows_dev[s], append_pos=self.append_pos)
+            self._pending = gat
+            if not distinct:
+                for _ in range(1, cfg.layers_per_group):
+                    ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
+                                        stride, stream=main)
+
     def _step_pipelined(self, s: int):
         torch = self.torch
         cfg, ctx, n = self.cfg, self.ctx, self.n
@@ -409,6 +462,7 @@ class GpuRun:
         of pages without one first).  Returns device tensors (freed physical
         page or -1, status) per entry."""
         torch = self.torch
+        self.finish(stream)  # a pending gather may still read the pages
         n = len(plan)
         req = torch.tensor([r for r, _ in plan] or [0], dtype=torch.int32, device=self.dev)
         page = torch.tensor([p for _, p in plan] or [0], dtype=torch.int32, device=self.dev)
@@ -421,6 +475,7 @@ class GpuRun:
         """Enqueue making the (request, page, physical page) list ready.
         Returns the device status tensor per entry."""
         torch = self.torch
+        self.finish(stream)  # a pending gather may still read the pool
         n = len(placed)
         cols = list(zip(*placed)) if placed else [[0], [0], [0]]
         req, page, phys = (torch.tensor(list(c), dtype=torch.int32, device=self.dev) for c in cols)
@@ -448,7 +503,8 @@ class GpuRun:
         for dst, src in zip(self.tail, snap["tail"]):
             dst.copy_(src)
 
-    def capture(self, steps, prefetch_groups=0, fused: bool = False, pipelined: bool = False):
+    def capture(self, steps, prefetch_groups=0, fused: bool = False, pipelined: bool = False,
+                merged: bool = False):
         """Capture the launches of `steps` into one HIP graph (nothing runs
         until it is replayed).  Each replay runs those decode steps again from
         whatever state the buffers hold."""
@@ -474,12 +530,13 @@ class GpuRun:
                 with torch.cuda.graph(graph, stream=cap):
                     for s in steps:
                         self.step(s, prefetch_groups=prefetch_groups, fused=fused,
-                                  pipelined=pipelined)
-                    self.finish(cap)  # the side stream joins before the capture ends
+                                  pipelined=pipelined, merged=merged)
+                    # the last gather, and the side stream joins, before the capture ends
+                    self.finish(cap)
         finally:
             self._capturing = False
             self._events = []
-            self._gather_done, self._side_last = {}, None
+            self._gather_done, self._side_last, self._pending = {}, None, None
         torch.cuda.current_stream().wait_stream(cap)
         return graph
 
@@ -494,12 +551,14 @@ class GpuRun:
 
     # ------------------------------------------------------------------ read-back (syncs)
     def state(self) -> dict:
+        self.finish()
         self.torch.cuda.synchronize()
         return {"L": self.L.cpu().numpy(), "tag": self.tag.cpu().numpy(),
                 "stamp": self.stamp.cpu().numpy().view(np.uint32),
                 "clock": self.clock.cpu().numpy().view(np.uint32)}
 
     def group(self, g: int, with_out: bool = True) -> dict:
+        self.finish()
         self.torch.cuda.synchronize()
         rec = {"loc": self.loc[g].cpu().numpy().view(np.uint32),
                "fills": self.fills[g].cpu().numpy(),

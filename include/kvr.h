@@ -300,6 +300,66 @@ int kvr_fused_gather_append_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *
                                  int32_t *status, const void *new_rows, const int32_t *append_pos,
                                  void *stream);
 
+/* One fused gather, as the arguments of kvr_fused_gather_append_rows
+ * (new_rows and append_pos NULL: of kvr_fused_gather_rows).  layers and out
+ * are host arrays of n_layers entries; the other pointers as documented
+ * there. */
+typedef struct kvr_gather_call {
+    int32_t n_layers;
+    const int32_t *layers;
+    int32_t n;
+    const int32_t *req_ids;
+    const uint32_t *loc;
+    const int32_t *sel;
+    const int32_t *count;
+    int32_t stride;
+    void *const *out;
+    int32_t *status;
+    const void *new_rows;
+    const int32_t *append_pos;
+} kvr_gather_call;
+
+/* One resolve, as the arguments of kvr_append_resolve_rows_deferred
+ * (new_rows, append_status and append_pos NULL: of kvr_resolve_rows), with
+ * no host fill (fill_layer -1). */
+typedef struct kvr_resolve_call {
+    int32_t n;
+    const int32_t *req_ids;
+    const void *new_rows;
+    int32_t *append_status;
+    int32_t *append_pos;
+    const int32_t *sel;
+    const int32_t *sel_count;
+    int32_t stride;
+    uint32_t *loc;
+    kvr_fill *fills;
+    int32_t *fill_count;
+    int32_t *status;
+    kvr_stats *stats;
+} kvr_resolve_call;
+
+/* The gather of one resolved selection and the resolve of the next one (the
+ * next resolving layer's, or the next decode step's) in one launch ("How it
+ * works": the resolve of "Resolution" and the gather the location vector of
+ * "Model-specific reuse" feeds), so that the resolve leaves the critical
+ * path without a wait between two queues.  Same results as
+ * kvr_fused_gather_append_rows (or kvr_fused_gather_rows) with `gather`
+ * followed by kvr_append_resolve_rows_deferred (or kvr_resolve_rows) with
+ * `resolve`, provided the resolve writes none of the buffers the gather
+ * reads (its loc, sel, count, new_rows and append_pos: give the two calls
+ * different buffers, e.g. two sets used in turn).  The two never touch the
+ * same state otherwise: the resolve reads and writes metadata and writes the
+ * host copy of appended rows (beyond every row the gather fetches); the
+ * gather writes hot-cache slots, tails and outputs.  An append in `resolve`
+ * must be deferred (append_pos given): its tail slot may still be read by the
+ * gather.  Either call may be NULL (then this is the other call alone);
+ * argument errors of either half are returned before anything is launched.
+ * Calls on one stream run in order, so a decode loop issues, per resolving
+ * layer, this call with the previous layer's gather and this layer's
+ * resolve, and ends with the last gather alone. */
+int kvr_gather_resolve_rows(kvr_ctx *ctx, const kvr_gather_call *gather,
+                            const kvr_resolve_call *resolve, void *stream);
+
 /* Verification block dedup ("Speculative state": queries share missing-row
  * retrieval).  Per request: union_rows[i][0..u) = the distinct rows of the q
  * selections, ascending; map[i][qi][j] = index of sel[i][qi][j] in it.
@@ -492,6 +552,7 @@ typedef enum kvr_kernel {
     KVR_KERNEL_DEDUP = 4,
     KVR_KERNEL_STATE = 5,    /* state initialisation, location copies */
     KVR_KERNEL_FUSED = 6,    /* fill pass and resident gather in one launch */
+    KVR_KERNEL_STEP = 7,     /* a fused gather beside the next resolve */
 } kvr_kernel;
 
 int kvr_timing_begin(kvr_ctx *ctx, int32_t capacity);

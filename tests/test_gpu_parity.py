@@ -84,7 +84,7 @@ def _compare_state(gpu, run, reqs):
 
 
 def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0, fused=False,
-                fuse_append=True, pipelined=False):
+                fuse_append=True, pipelined=False, merged=False):
     inputs = Inputs(cfg, max_new=max_new)
     reqs = list(range(cfg.n_req)) if reqs is None else list(reqs)
     pool = []
@@ -102,7 +102,8 @@ def _run_parity(cfg, reqs=None, check_hot=True, max_new=None, prefetch_groups=0,
             o = run.step(s, sels=[x[reqs] for x in sels])
             # groups of one step share buffers per group, so run the GPU step and
             # read every group back afterwards
-            gpu.step(s, prefetch_groups=prefetch_groups, fused=fused, pipelined=pipelined)
+            gpu.step(s, prefetch_groups=prefetch_groups, fused=fused, pipelined=pipelined,
+                     merged=merged)
             st = gpu.state()
             assert (st["L"] == inputs.length_at(s)).all()
             assert (gpu.append_status.cpu().numpy() == 0).all()
@@ -204,17 +205,25 @@ def test_fused_repeated_rows():
         gpu.close()
 
 
-@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
-def test_pipelined_schedule_parity(c):
-    """The pipelined schedule (resolves on the current stream, fused launches
-    on a side stream, the append's tail write deferred to the step's first
-    fused launch): the oracle's results at every step."""
-    _run_parity(tiny(c), fused=True, pipelined=True)
+_OVERLAP = [dict(pipelined=True), dict(merged=True)]
+_OVERLAP_IDS = ["pipelined", "merged"]
 
 
+@pytest.mark.parametrize("kw", _OVERLAP, ids=_OVERLAP_IDS)
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
-def test_pipelined_schedule_back_to_back(c):
-    """All steps of the pipelined schedule issued with no host wait between
+def test_pipelined_schedule_parity(c, kw):
+    """The schedules that overlap each resolve with the previous gathers --
+    pipelined (resolves on the current stream, fused launches on a side
+    stream) and merged (one launch per resolve, beside the previous
+    resolve's gather) -- with the append's tail write deferred to the step's
+    first gather: the oracle's results at every step."""
+    _run_parity(tiny(c), fused=True, **kw)
+
+
+@pytest.mark.parametrize("kw", _OVERLAP, ids=_OVERLAP_IDS)
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_pipelined_schedule_back_to_back(c, kw):
+    """All steps of an overlapping schedule issued with no host wait between
     them, so each step's resolve runs beside the previous step's gathers;
     after the last step its outputs, the metadata, the tails and the hot
     payload equal the oracle's."""
@@ -227,7 +236,7 @@ def test_pipelined_schedule_back_to_back(c):
     try:
         gpu.stage(range(cfg.steps))
         for s in range(cfg.steps):
-            gpu.step(s, fused=True, pipelined=True)
+            gpu.step(s, fused=True, **kw)
             o = run.step(s)
         gpu.finish()
         torch.cuda.synchronize()
@@ -244,13 +253,17 @@ def test_pipelined_schedule_back_to_back(c):
         gpu.close()
 
 
-def test_pipelined_edges():
-    """The pipelined schedule without a tail, with one-row pages, with tight
-    budgets (failed requests) and with selections that name the newest row
-    (the one whose tail write is deferred) in every step."""
-    _run_parity(tiny(2).with_(T=0, steps=4), fused=True, pipelined=True)
-    _run_parity(tiny(4).with_(P=1, steps=4), fused=True, pipelined=True)
-    _run_parity(tiny(3).with_(B=160), fused=True, pipelined=True)
+@pytest.mark.parametrize("kw", _OVERLAP, ids=_OVERLAP_IDS)
+def test_pipelined_edges(kw):
+    """The overlapping schedules without a tail, with one-row pages, with
+    tight budgets (failed requests), with more layers than one launch takes,
+    and with selections that name the newest row (the one whose tail write
+    is deferred) in every step."""
+    _run_parity(tiny(2).with_(T=0, steps=4), fused=True, **kw)
+    _run_parity(tiny(4).with_(P=1, steps=4), fused=True, **kw)
+    _run_parity(tiny(3).with_(B=160), fused=True, **kw)
+    _run_parity(tiny(2).with_(name="many_layers", payload_layers=26, R=16, steps=3), fused=True,
+                **kw)
     cfg = tiny(2).with_(steps=5)
     inputs = Inputs(cfg, max_new=cfg.steps)
     gpu = _gpu_run(inputs)
@@ -265,7 +278,7 @@ def test_pipelined_edges():
             sels = [sel]
             gpu.stage([s], sels={s: sels})
             o = run.step(s, sels=sels)
-            gpu.step(s, fused=True, pipelined=True)
+            gpu.step(s, fused=True, **kw)
             _compare_group(cfg, gpu.group(0), o["groups"][0], reqs)
             _compare_state(gpu, run, reqs)
         for l in range(cfg.payload_layers):
@@ -351,6 +364,114 @@ def test_deferred_append_entry_points_equal_plain_ones():
                 assert np.array_equal(a["hot"][l], b["hot"][l]), l
                 assert np.array_equal(a["host"][l], b["host"][l]), l
             assert a["stats"] == b["stats"]
+    finally:
+        for g in runs:
+            g.close()
+
+
+def test_gather_resolve_entry_point_equals_separate_calls():
+    """kvr_gather_resolve_rows(gather of step s-1, resolve of step s) against
+    the separate calls (kvr_append_resolve_rows_deferred then
+    kvr_fused_gather_append_rows per step) on two copies of one state, over
+    five steps with a permuted request list, a request at capacity, the
+    newest row selected, and an empty selection in one step: every step's
+    locations, fills, statuses, appended positions and gathered rows, and
+    the final metadata, tails, hot payload, host rows and counters are
+    equal.  Also the argument errors of the combined call."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2).with_(steps=5)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    runs = [_gpu_run(inputs), _gpu_run(inputs)]
+    n, k, S = cfg.n_req, cfg.k, cfg.steps
+    layers = list(range(cfg.payload_layers))
+    perm = [2, 0, 1]
+    dev = "cuda"
+    try:
+        for g in runs:
+            g.stage(range(S))
+            g.L[1] = inputs.host_rows
+        req = torch.tensor(perm, dtype=torch.int32, device=dev)
+        sels, counts = [], []
+        for s in range(S):
+            sel = runs[0].sel_dev[s][0][perm].reshape(n, k).contiguous()
+            sel[0, 0] = inputs.length_at(s) - 1
+            sels.append(sel)
+            counts.append(torch.full((n,), 0 if s == 2 else k, dtype=torch.int32, device=dev))
+
+        def buffers():
+            return dict(ast=torch.full((n,), 99, dtype=torch.int32, device=dev),
+                        apos=torch.full((n,), 77, dtype=torch.int32, device=dev),
+                        loc=torch.zeros((n, k), dtype=torch.int32, device=dev),
+                        fills=torch.zeros((n, cfg.B, 2), dtype=torch.int32, device=dev),
+                        fc=torch.zeros(n, dtype=torch.int32, device=dev),
+                        st=torch.zeros(n, dtype=torch.int32, device=dev),
+                        gst=torch.zeros(n, dtype=torch.int32, device=dev),
+                        outs=[torch.full((n, k, cfg.R), 0xEE, dtype=torch.uint8, device=dev)
+                              for _ in layers])
+
+        bufs = [[buffers() for _ in range(S)] for _ in runs]
+        a, b = runs
+        for s in range(S):
+            x = bufs[0][s]
+            a.ctx.append_resolve_rows_deferred(n, req, a.rows_dev[s], x["ast"], x["apos"], sels[s],
+                                               counts[s], k, x["loc"], x["fills"], x["fc"], -1,
+                                               x["st"], a.stats)
+            a.ctx.fused_gather_append_rows(layers, n, req, x["loc"], sels[s], counts[s], k,
+                                           x["outs"], a.rows_dev[s], x["apos"], x["gst"])
+
+        def res_call(s):
+            y = bufs[1][s]
+            return dict(n=n, req_ids=req, new_rows=b.rows_dev[s], append_status=y["ast"],
+                        append_pos=y["apos"], sel=sels[s], sel_count=counts[s], stride=k,
+                        loc=y["loc"], fills=y["fills"], fill_count=y["fc"], status=y["st"],
+                        stats=b.stats)
+
+        def gat_call(s):
+            y = bufs[1][s]
+            return dict(layers=layers, n=n, req_ids=req, loc=y["loc"], sel=sels[s],
+                        count=counts[s], stride=k, outs=y["outs"], status=y["gst"],
+                        new_rows=b.rows_dev[s], append_pos=y["apos"])
+
+        with pytest.raises(kvr.KvrError):
+            b.ctx.gather_resolve_rows(None, None)
+        bad = res_call(0)
+        bad["append_pos"] = None
+        with pytest.raises(kvr.KvrError):
+            b.ctx.gather_resolve_rows(None, bad)
+        bad = gat_call(0)
+        bad["append_pos"] = None
+        with pytest.raises(kvr.KvrError):
+            b.ctx.gather_resolve_rows(bad, res_call(0))
+        bad = gat_call(0)
+        bad["layers"] = layers[:-1]
+        bad["outs"] = bad["outs"][:-1]
+        with pytest.raises(kvr.KvrError):
+            b.ctx.gather_resolve_rows(bad, res_call(0))
+        torch.cuda.synchronize()
+        # the refused calls ran nothing (request 1 was put at capacity above)
+        assert b.state()["L"].tolist() == [cfg.H, inputs.host_rows, cfg.H]
+        for s in range(S + 1):
+            b.ctx.gather_resolve_rows(gat_call(s - 1) if s > 0 else None,
+                                      res_call(s) if s < S else None)
+        torch.cuda.synchronize()
+        for s in range(S):
+            x, y = bufs[0][s], bufs[1][s]
+            for key in ("ast", "apos", "loc", "fc", "st", "gst"):
+                assert torch.equal(x[key], y[key]), (s, key)
+            fc = x["fc"].cpu().numpy()
+            for i in range(n):
+                assert torch.equal(x["fills"][i, :fc[i]], y["fills"][i, :fc[i]]), (s, i)
+            for l in layers:
+                assert torch.equal(x["outs"][l], y["outs"][l]), (s, l)
+        sa, sb = a.state(), b.state()
+        for key in sa:
+            assert np.array_equal(sa[key], sb[key]), key
+        for l in layers:
+            assert torch.equal(a.tail[l], b.tail[l])
+            assert torch.equal(a.hot[l], b.hot[l])
+            assert np.array_equal(a.host[l], b.host[l])
+        assert a.stats_dict() == b.stats_dict()
     finally:
         for g in runs:
             g.close()
@@ -1067,7 +1188,9 @@ _CAPTURE_CRASH = ("capturing the fused schedule for one physical source (in an e
     (2, 0, False, False), (2, 2, False, False), (5, 2, False, False), (4, 2, False, False),
     (2, 0, True, False),
     pytest.param(5, 0, True, False, marks=pytest.mark.skip(reason=_CAPTURE_CRASH)),
-    (4, 0, True, False), (1, 0, True, True), (2, 0, True, True), (4, 0, True, True)])
+    (4, 0, True, False), (1, 0, True, "pipelined"), (2, 0, True, "pipelined"),
+    (4, 0, True, "pipelined"), (1, 0, True, "merged"), (2, 0, True, "merged"),
+    (4, 0, True, "merged")])
 def test_graph_replays_match_oracle(shape, prefetch_groups, fused, pipelined):
     """Decode steps captured into HIP graphs give the oracle's results: a
     multi-step graph replayed once, then a one-step graph replayed three times
@@ -1086,7 +1209,8 @@ def test_graph_replays_match_oracle(shape, prefetch_groups, fused, pipelined):
         _compare_state(gpu, run, reqs)
 
     try:
-        kw = dict(prefetch_groups=prefetch_groups, fused=fused, pipelined=pipelined)
+        kw = dict(prefetch_groups=prefetch_groups, fused=fused,
+                  pipelined=pipelined == "pipelined", merged=pipelined == "merged")
         gpu.stage(range(cfg.steps))
         gpu.step(0, **kw)
         compare(run.step(0))
@@ -1119,8 +1243,8 @@ def test_bench_configuration_parity(c):
     import bench
     cfg = FULL[c].with_(steps=32)
     schedule = bench.auto_schedule(cfg)
-    fused, pipelined = schedule in ("fused", "pipelined"), schedule == "pipelined"
-    assert not (fused and cfg.reuse != "distinct")  # captured, as bench.py does
+    kw = bench.schedule_kwargs(schedule)
+    assert not (kw["fused"] and cfg.reuse != "distinct")  # captured, as bench.py does
     warm, pg = 4, 2
     inputs = Inputs(cfg, max_new=cfg.steps)
     print(f"[bench-config] {cfg.name}: {schedule}", flush=True)
@@ -1130,12 +1254,11 @@ def test_bench_configuration_parity(c):
     try:
         gpu.stage(range(cfg.steps))
         for s in range(warm):
-            gpu.step(s, prefetch_groups=pg, fused=fused, pipelined=pipelined)
+            gpu.step(s, prefetch_groups=pg, **kw)
         gpu.finish()
         torch.cuda.synchronize()
         snap = gpu.snapshot()
-        graph = gpu.capture(range(warm, cfg.steps), prefetch_groups=pg, fused=fused,
-                            pipelined=pipelined)
+        graph = gpu.capture(range(warm, cfg.steps), prefetch_groups=pg, **kw)
         torch.cuda.synchronize()
         for s in range(cfg.steps):
             o = run.step(s)
@@ -1169,8 +1292,8 @@ def test_bench_configuration_parity_long_context():
     import bench
     cfg = FULL[5].with_(steps=32)
     schedule = bench.auto_schedule(cfg)
-    fused, pipelined = schedule in ("fused", "pipelined"), schedule == "pipelined"
-    assert fused and cfg.reuse != "distinct"
+    kw = bench.schedule_kwargs(schedule)
+    assert kw["fused"] and cfg.reuse != "distinct"
     warm = 4
     reqs = [0, 1, 42, 63]
     inputs = Inputs(cfg, max_new=cfg.steps)
@@ -1197,19 +1320,19 @@ def test_bench_configuration_parity_long_context():
     try:
         gpu.stage(range(cfg.steps))
         for s in range(warm):
-            gpu.step(s, fused=fused, pipelined=pipelined)
+            gpu.step(s, **kw)
             o = run.step(s)
         torch.cuda.synchronize()
         compare(o)
         snap = gpu.snapshot()
         for s in range(warm, cfg.steps):
-            gpu.step(s, fused=fused, pipelined=pipelined)
+            gpu.step(s, **kw)
             o = run.step(s)
             compare(o)
         print(f"[bench-config] {cfg.name}: step by step ok", flush=True)
         gpu.restore(snap)
         for s in range(warm, cfg.steps):
-            gpu.step(s, fused=fused, pipelined=pipelined)
+            gpu.step(s, **kw)
         gpu.finish()
         torch.cuda.synchronize()
         compare(o)
