@@ -68,7 +68,7 @@ def parse():
                          "included) runs beside the previous gathers; merged: the same overlap "
                          "in one launch per resolve (gather of the previous resolve beside "
                          "it) on one stream; prefetch: fills in layer groups ahead of "
-                         "per-group gathers; auto: see auto_schedule()")
+                         "per-group gathers; auto: merged")
     ap.add_argument("--step-buffers", type=int, default=0,
                     help="sets of per-step output buffers (0: the runner's default)")
     ap.add_argument("--repeats", type=int, default=5,
@@ -119,28 +119,14 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def auto_fused(cfg) -> bool:
-    """The default schedule: fused where several payload layers share the
-    indices (their resident gathers are big enough to hide under the fill
-    pass) or one physical source serves several resolving layers (each
-    layer's gather leaves the chain of fills); with one payload layer and one
-    resolve the refill in ascending row order reads the host faster, unless
-    the call is so small that latency rules (a launch fewer then counts most).
-    """
-    return ((cfg.reuse == "distinct" and cfg.payload_layers > 1)
-            or (cfg.reuse != "distinct" and cfg.groups > 1)
-            or cfg.n_req * cfg.sel_cap <= 4096)
-
-
 def auto_schedule(cfg) -> str:
-    """The default schedule: where the fused schedule is the default
-    (auto_fused), a form whose resolves leave the critical path: merged (one
-    launch per resolve, beside the previous gather) except for verify blocks,
-    whose large resident gather runs slower in the merged launch's
-    1024-thread workgroups, which take the pipelined form; else prefetch."""
-    if not auto_fused(cfg):
-        return "prefetch"
-    return "pipelined" if cfg.q > 1 else "merged"
+    """The default schedule: merged (each resolve in one launch with the
+    gather of the resolve before it), which measured fastest or even on
+    every workload: single request 11.0 us per step (fused 16.6), GLM
+    221 us (fused 241), memory pressure 2.247 ms (prefetch 2.311), verify
+    0.704 ms (pipelined 0.704, fused 0.733), long context 2.886 ms (fused
+    2.977)."""
+    return "merged"
 
 
 def schedule_kwargs(schedule: str) -> dict:
@@ -217,16 +203,18 @@ def host_link_gbs(torch, nbytes=1 << 30, reps=5):
     return best
 
 
-# Counter-based HBM traffic of the gather kernel on the shared-indices GLM
-# workload.  The summary records the hash of the kernel source it was taken
-# with; once the source changes the figure no longer applies and is dropped.
-TRAFFIC_PROFILES = os.path.join(ROOT, "profiles", "gather_kernel_*_traffic.md")
+# Counter-based memory traffic of the gathering kernels (the resident gather
+# alone, the step kernel), one summary per workload and kernel.  A summary
+# records the hash of the kernel sources it was taken with; once they change
+# the figure no longer applies and is dropped.
+TRAFFIC_PROFILES = os.path.join(ROOT, "profiles", "*_traffic.md")
 GATHER_SOURCES = [os.path.join(ROOT, "hierarchical_sparse_kv_resolve_amd", "csrc", name)
-                  for name in ("gather.hip", "rows.h")]
+                  for name in ("gather.hip", "gather_body.h", "rows.h", "step.hip",
+                               "resolve_body.h", "block.h")]
 
 
 def gather_source_hash():
-    """sha256 over the gather kernel's source files, in order."""
+    """sha256 over the gathering kernels' source files, in order."""
     import hashlib
     h = hashlib.sha256()
     for path in GATHER_SOURCES:

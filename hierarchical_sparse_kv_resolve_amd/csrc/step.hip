@@ -24,11 +24,16 @@ namespace {
 
 constexpr int NTS = 1024;
 // Fill workers per launch (over all its layers) and 16-byte host loads in
-// flight per lane: 32 workgroups of 1024 threads with 8 loads each keep as
-// many bytes in flight as the fused kernel's 128 workgroups of 256 threads
-// with 16, within the 128 registers a lane of a 1024-thread workgroup has.
-constexpr int kStepFillWorkers = 32;
-constexpr int kStepFillUnroll = 8;
+// flight per lane, within the 128 registers a lane of a 1024-thread
+// workgroup has (16 loads spill).  Measured on the long-context and GLM
+// shapes (ms per step / us per step): 32 workers with 8 loads 2.939 / 221.1,
+// 48 x 8 2.913 / 221.0, 64 x 8 2.908 / 220.7, 32 x 12 2.920 / 220.6,
+// 48 x 12 2.915 / 220.8, 64 x 12 2.887-2.889 / 221.0-221.6, 96 x 12 2.922 /
+// 238.3, 128 x 12 2.974 / 262.1: more workers than 64 take compute units the
+// resident tiles and the resolve need (one 1024-thread workgroup fits a
+// compute unit beside the resolve's LDS).
+constexpr int kStepFillWorkers = 64;
+constexpr int kStepFillUnroll = 12;
 
 struct StepLayout {
     int32_t n_fill;         // fill workers: workers * nt

@@ -59,6 +59,7 @@ def _group_sampled(gpu, g, reqs):
     """The GPU's group record for `reqs` only (read back on the device side
     first, so a full-size run copies little), marked local."""
     import torch
+    gpu.finish()  # the last gather of a merged schedule is issued here
     gpu.torch.cuda.synchronize()
     idx = torch.tensor(reqs, dtype=torch.long, device=gpu.dev)
 
