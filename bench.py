@@ -654,7 +654,7 @@ def main():
         roofline = {"bound": "host_link", "achieved": round(host_gbs, 1),
                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
                     "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4),
-                    "traffic": recorded_traffic(cfg.name, "fused" if fused else
+                    "traffic": recorded_traffic(cfg.name, schedule if fused else
                                                 f"prefetch:{args.prefetch_groups}", d_kernel),
                     "kernel": d_kernel, "bytes_per_launch": int(d_host),
                     "launch_us": round(d_ms * 1e3, 2), "launches": n_launch,

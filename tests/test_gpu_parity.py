@@ -497,7 +497,8 @@ def test_hot_budget_parity_full_size(c, B, reqs):
 def test_random_shapes_parity(seed):
     """Seeded random reduced shapes (history, page and tail sizes, budgets
     from tight to roomy, row sizes, request, layer and group counts, verify
-    blocks) on the one-stream, fused and prefetch schedules."""
+    blocks) on the one-stream, fused, prefetch, merged and pipelined
+    schedules."""
     rng = np.random.default_rng(1000 + seed)
     base = tiny([2, 4, 5][seed % 3])
     H = int(rng.integers(200, 3000))
@@ -513,7 +514,8 @@ def test_random_shapes_parity(seed):
         kw["groups"] = int(rng.integers(1, 4))
     cfg = base.with_(**kw)
     print(f"[parity] random shape {cfg}", flush=True)
-    for sched in (dict(), dict(fused=True), dict(prefetch_groups=2)):
+    for sched in (dict(), dict(fused=True), dict(prefetch_groups=2),
+                  dict(fused=True, merged=True), dict(fused=True, pipelined=True)):
         _run_parity(cfg, **sched)
 
 
