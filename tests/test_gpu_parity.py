@@ -529,6 +529,7 @@ def test_long_history_parity(c, kw):
                         ready_frac=0.0, steps=4, payload_layers=1, **kw)
     _run_parity(cfg)
     _run_parity(cfg, fused=True)
+    _run_parity(cfg, fused=True, merged=True)
 
 
 def test_more_layers_than_one_launch_takes():
@@ -1409,7 +1410,9 @@ def test_launch_timing_records_each_kernel():
         gpu.close()
 
 
-@pytest.mark.parametrize("c,kw", [(2, dict()), (4, dict(fused=True)), (5, dict(prefetch_groups=2))])
+@pytest.mark.parametrize("c,kw", [(2, dict()), (4, dict(fused=True)), (5, dict(prefetch_groups=2)),
+                                  (2, dict(fused=True, merged=True)),
+                                  (5, dict(fused=True, merged=True))])
 def test_snapshot_resume_equals_continuous_run(c, kw):
     """Copy the state after step s, scramble it, restore it and run steps
     s..S-1: every output and the final state equal those of the continuous

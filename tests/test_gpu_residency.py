@@ -105,7 +105,11 @@ def test_page_moves_alone(c):
         gpu.close()
 
 
-def _load_step(cfg, reqs, deficit, bound, admit_at, drain_at, prefetch_groups=0):
+def _load_step(cfg, reqs, deficit, bound, admit_at, drain_at, prefetch_groups=0, sched=None,
+               every_step=True):
+    """every_step=False compares only after the last step, so that with the
+    merged schedule each page move is issued while the previous step's last
+    gather is still pending (the runner issues it first)."""
     from hierarchical_sparse_kv_resolve_amd import kvr
     inputs = Inputs(cfg, max_new=cfg.steps)
     gpu = _gpu_run(inputs)
@@ -142,12 +146,13 @@ def _load_step(cfg, reqs, deficit, bound, admit_at, drain_at, prefetch_groups=0)
             sels = [inputs.selections(s, g) for g in range(cfg.groups)]
             gpu.stage([s], sels={s: sels})
             o = run.step(s, sels=[x[reqs] for x in sels])
-            gpu.step(s, prefetch_groups=prefetch_groups)
-            for g in range(cfg.groups):
-                _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
-                assert (o["groups"][g]["status"] == 0).all()
-            _compare_state(gpu, run, reqs)
-            _compare_pages(cfg, gpu, run, reqs)
+            gpu.step(s, prefetch_groups=prefetch_groups, **(sched or {}))
+            if every_step or s == cfg.steps - 1:
+                for g in range(cfg.groups):
+                    _compare_group(cfg, gpu.group(g), o["groups"][g], reqs)
+                    assert (o["groups"][g]["status"] == 0).all()
+                _compare_state(gpu, run, reqs)
+                _compare_pages(cfg, gpu, run, reqs)
             assert (run.src.check() == 0).all()
         assert moved > 0
     finally:
@@ -159,6 +164,17 @@ def _load_step(cfg, reqs, deficit, bound, admit_at, drain_at, prefetch_groups=0)
 def test_load_step_matches_oracle(c, deficit, bound):
     cfg = tiny(c).with_(pool_spare=5, steps=8)
     _load_step(cfg, list(range(cfg.n_req)), deficit, bound, admit_at=2, drain_at=4)
+
+
+@pytest.mark.parametrize("every_step", [True, False])
+@pytest.mark.parametrize("c,deficit,bound", [(2, 8, 2), (5, 20, 4)])
+def test_load_step_merged_schedule(c, deficit, bound, every_step):
+    """Page reclaim and refill between steps of the merged schedule, whose
+    last gather of a step is still pending when the page moves are issued
+    (compared after every step, or only after the last)."""
+    cfg = tiny(c).with_(pool_spare=5, steps=8)
+    _load_step(cfg, list(range(cfg.n_req)), deficit, bound, admit_at=2, drain_at=4,
+               sched=dict(fused=True, merged=True), every_step=every_step)
 
 
 def test_load_step_full_glm_sampled():
