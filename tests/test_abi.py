@@ -74,6 +74,42 @@ def test_hot_path_calls_reject_a_null_context():
         assert "null context" in kvr.last_error()
 
 
+def test_deferred_and_combined_calls_reject_bad_arguments_on_the_host():
+    """The deferred-append pair and the combined gather-resolve call refuse a
+    null context, and the combined call refuses being given neither half,
+    before any device work."""
+    lib = kvr.lib()
+    layers = (ctypes.c_int32 * 1)(0)
+    outs = (ctypes.c_void_p * 1)(None)
+    assert lib.kvr_append_resolve_rows_deferred(None, 0, None, None, None, None, None, None, 0,
+                                                None, None, None, -1, None, None,
+                                                None) == kvr.E_ARG
+    assert "null context" in kvr.last_error()
+    assert lib.kvr_fused_gather_append_rows(None, 1, layers, 0, None, None, None, None, 0, outs,
+                                            None, None, None, None) == kvr.E_ARG
+    assert "null context" in kvr.last_error()
+    assert lib.kvr_gather_resolve_rows(None, None, None, None) == kvr.E_ARG
+    assert "gather or a resolve" in kvr.last_error()
+    g = kvr.GatherCall(1, ctypes.addressof(layers), 0, None, None, None, None, 0,
+                       ctypes.addressof(outs), None, None, None)
+    assert lib.kvr_gather_resolve_rows(None, ctypes.byref(g), None, None) == kvr.E_ARG
+    assert "null context" in kvr.last_error()
+    r = kvr.ResolveCall(0, None, None, None, None, None, None, 0, None, None, None, None, None)
+    assert lib.kvr_gather_resolve_rows(None, None, ctypes.byref(r), None) == kvr.E_ARG
+    assert "null context" in kvr.last_error()
+
+
+def test_call_structs_match_the_header():
+    """The binding's ctypes mirrors of kvr_gather_call and kvr_resolve_call
+    have the header's field names in the header's order."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvr.h")).read(),
+                  flags=re.S)
+    for struct, cls in (("kvr_gather_call", kvr.GatherCall), ("kvr_resolve_call", kvr.ResolveCall)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), text, re.S).group(1)
+        fields = re.findall(r"(\w+);", body)
+        assert fields == [name for name, _ in cls._fields_], struct
+
+
 def test_kernel_kinds_match_the_binding():
     text = open(os.path.join(ROOT, "include", "kvr.h")).read()
     kinds = {name.lower(): int(v) for name, v in re.findall(r"KVR_KERNEL_([A-Z]+)\s*=\s*(\d+)", text)}
