@@ -478,6 +478,25 @@ def test_gather_resolve_entry_point_equals_separate_calls():
             g.close()
 
 
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+@pytest.mark.parametrize("ek", [1, 2, 4, 8])
+def test_every_resolve_instance(ek, eb):
+    """Every compiled instance of the resolve (selection entries and hot
+    slots per thread of its 1024-thread workgroup: 1, 2, 4 or 8 each), in
+    the resolve kernel and in the step kernel: a selection capacity just
+    under ek * 1024 and a budget just under eb * 1024, on the one-stream,
+    fused and merged schedules."""
+    k, B = ek * 1024 - 37, eb * 1024 - 5
+    # enough ready pages that the pending rows mostly fit the budget, so the
+    # victim selection runs (a few calls may still fail with E_CAPACITY)
+    ready = min(0.97, max(0.7, 1.0 - 0.7 * B / k))
+    cfg = tiny(2).with_(name=f"inst{ek}x{eb}", n_req=2, H=24000, T=100, k=k, B=B,
+                        payload_layers=1, R=32, steps=3, sel="uniform", ready_frac=ready)
+    print(f"[parity] instance {ek}x{eb}: k={k} B={B}", flush=True)
+    for sched in (dict(), dict(fused=True), dict(fused=True, merged=True)):
+        _run_parity(cfg, **sched)
+
+
 @pytest.mark.parametrize("c,B", [(2, 80), (2, 512), (3, 160), (3, 1024), (5, 120), (5, 2048)])
 def test_hot_budget_parity(c, B):
     """Hot-cache budgets below and above the reduced shapes' own: a tight
