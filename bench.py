@@ -506,6 +506,16 @@ def main():
         if merged:
             # each launch but the last gathers one selection beside the next resolve
             launches["step"] = rec.get("step", [])
+        # Pass 1c: the plain calls over the same steps (resolve_rows with its
+        # host fill, then one gather_rows of every row), so that the gather
+        # call of the boundary is timed on its own as well
+        gpu.restore(snap)
+        gpu.ctx.timing_begin(64 * K + 64)
+        for s in range(W, total):
+            gpu.step(s, serialize=True)
+        gpu.finish()
+        plain_gathers = launch_means_ms(gpu.ctx.timing_end()).get("gather", [])
+        torch.cuda.synchronize()
     if not no_graph:
         gpu.restore(snap)
         graph = gpu.capture(range(W, total), **kw)
@@ -665,6 +675,21 @@ def main():
         roofline = dict(hbm_part, bound="hbm", kernel=d_kernel, launch_us=round(d_ms * 1e3, 2),
                         launches=n_launch, traffic=gather_alone["traffic"], timing=d_timing)
     roofline["gather_alone"] = gather_alone
+    if fused and plain_gathers:
+        # every row of every entry moved (fresh rows from their hot slots)
+        a_bytes = (entries * 2 * cfg.R * n_out + entries * 4) / len(plain_gathers)
+        a_ms = sum(plain_gathers) / len(plain_gathers)
+        a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+        roofline["gather_rows"] = {
+            "kernel": "gather_kernel<all>", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": int(a_bytes), "launch_us": round(a_ms * 1e3, 2),
+            "launches": len(plain_gathers),
+            "frac_of_device_copy": round(a_gbs / dev_copy, 4),
+            "timing": "start/end events of each gather_rows dispatch in an eager pass of the "
+                      "plain calls (resolve_rows with its host fill, then gather_rows of every "
+                      "row) over the same timed steps from the same starting state, no two "
+                      "kernels overlapping"}
 
     found = max(1, stats["tail"] + stats["page"] + stats["hit"] + stats["miss"])
     split = {"step1_tail_or_page": round((stats["tail"] + stats["page"]) / found, 4),
