@@ -441,20 +441,17 @@ static int check_gather(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, i
     return KVR_OK;
 }
 
-static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
-                        int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
-                        const int32_t *count, int32_t stride, void *const *out, int32_t *status,
-                        void *stream, const void *new_rows = nullptr,
-                        const int32_t *append_pos = nullptr)
+// The launches of a gather whose arguments are checked: one per group of up
+// to kGatherLayersPerLaunch layers (with deferred appends a launch runs even
+// for an empty selection: it still writes the appended rows).
+static int gather_launch(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
+                         int32_t n, const int32_t *req_ids, const uint32_t *loc,
+                         const int32_t *sel, const int32_t *count, int32_t stride,
+                         void *const *out, int32_t *status, hipStream_t s, const void *new_rows,
+                         const int32_t *append_pos)
 {
-    if (int rc = check_gather(ctx, n_layers, layers, n, loc, stride, out, new_rows, append_pos))
-        return rc;
     const bool deferred = append_pos != nullptr;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = check_stream(ctx, s);
-    // one launch per group of up to kGatherLayersPerLaunch layers (with
-    // deferred appends a launch runs even for an empty selection: it still
-    // writes the appended rows)
+    int rc = KVR_OK;
     kvr::GatherTarget targets[kvr::kGatherLayersPerLaunch];
     for (int32_t t0 = 0; rc == KVR_OK && n > 0 && (stride > 0 || deferred) && t0 < n_layers;
          t0 += kvr::kGatherLayersPerLaunch) {
@@ -471,6 +468,21 @@ static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int3
             rc = hip_fail(e, "gather launch");
     }
     return rc == KVR_OK ? ok() : rc;
+}
+
+static int gather_entry(kvr_ctx *ctx, int32_t mode, int32_t n_layers, const int32_t *layers,
+                        int32_t n, const int32_t *req_ids, const uint32_t *loc, const int32_t *sel,
+                        const int32_t *count, int32_t stride, void *const *out, int32_t *status,
+                        void *stream, const void *new_rows = nullptr,
+                        const int32_t *append_pos = nullptr)
+{
+    if (int rc = check_gather(ctx, n_layers, layers, n, loc, stride, out, new_rows, append_pos))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int rc = check_stream(ctx, s))
+        return rc;
+    return gather_launch(ctx, mode, n_layers, layers, n, req_ids, loc, sel, count, stride, out,
+                         status, s, new_rows, append_pos);
 }
 
 int kvr_gather_rows(kvr_ctx *ctx, int32_t n_layers, const int32_t *layers, int32_t n,
@@ -578,10 +590,12 @@ int kvr_gather_resolve_rows(kvr_ctx *ctx, const kvr_gather_call *g, const kvr_re
     e = kvr::launch_step(ctx, *g, targets, nt0, *r, s);
     if (e != hipSuccess)
         return hip_fail(e, "gather-resolve launch");
+    // (the whole layer list was checked above: a deferred append names every
+    // layer once, and these launches write the tails of the layers after nt0)
     if (g->n_layers > nt0)
-        return gather_entry(ctx, kvr::kGatherFused, g->n_layers - nt0, g->layers + nt0, g->n,
-                            g->req_ids, g->loc, g->sel, g->count, g->stride, g->out + nt0,
-                            g->status, stream, g->new_rows, g->append_pos);
+        return gather_launch(ctx, kvr::kGatherFused, g->n_layers - nt0, g->layers + nt0, g->n,
+                             g->req_ids, g->loc, g->sel, g->count, g->stride, g->out + nt0,
+                             g->status, s, g->new_rows, g->append_pos);
     return ok();
 }
 

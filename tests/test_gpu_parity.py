@@ -228,8 +228,20 @@ def test_pipelined_schedule_back_to_back(c, kw):
     them, so each step's resolve runs beside the previous step's gathers;
     after the last step its outputs, the metadata, the tails and the hot
     payload equal the oracle's."""
+    _back_to_back(tiny(c).with_(steps=8), kw)
+
+
+@pytest.mark.parametrize("kw", _OVERLAP, ids=_OVERLAP_IDS)
+def test_back_to_back_more_layers_than_one_launch(kw):
+    """26 payload layers with no host wait between steps: the merged
+    schedule's gather-resolve launch takes the first 24 layers beside the
+    resolve and a fused launch of its own the last 2 (deferred appends
+    included); both schedules equal the oracle."""
+    _back_to_back(tiny(2).with_(name="many_layers", payload_layers=26, R=16, steps=4), kw)
+
+
+def _back_to_back(cfg, kw):
     import torch
-    cfg = tiny(c).with_(steps=8)
     inputs = Inputs(cfg, max_new=cfg.steps)
     gpu = _gpu_run(inputs)
     run = OracleRun(inputs)
