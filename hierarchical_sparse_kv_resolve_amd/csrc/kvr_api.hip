@@ -98,7 +98,8 @@ int check_n(const kvr_ctx *c, int32_t n)
     return KVR_OK;
 }
 
-// The stream must belong to the context's device.
+// The current device and the stream (the null stream: the current device's)
+// must be the context's device.
 int check_stream(const kvr_ctx *c, hipStream_t s)
 {
     int dev = -1;
@@ -107,7 +108,15 @@ int check_stream(const kvr_ctx *c, hipStream_t s)
         return hip_fail(e, "hipGetDevice");
     if (dev != c->device)
         return fail(KVR_E_ARG, "current device %d is not the context's device %d", dev, c->device);
-    (void)s;
+    if (s) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(s, &sdev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamGetDevice");
+        if (sdev != c->device)
+            return fail(KVR_E_ARG, "the stream is on device %d, not the context's device %d",
+                        (int)sdev, c->device);
+    }
     return KVR_OK;
 }
 
