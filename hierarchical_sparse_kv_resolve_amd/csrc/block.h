@@ -27,24 +27,87 @@ __device__ __forceinline__ int ballot_rank(uint64_t mask)
     return __popcll(mask & ((1ull << lane_id()) - 1ull));
 }
 
+// DPP controls of gfx9: within one instruction a lane reads another lane of
+// its row of 16 (quad permutations, the mirror of each half row and of each
+// row, shifts right inside a row) or the last lane of an earlier row, with no
+// trip through LDS.  A lane whose source lies outside its row, and every lane
+// of a row left out by the row mask, reads 0.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowShr1 = 0x111;       // lane - 1 of the row
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140;     // lane 15 - i of the row
+constexpr int kDppRowHalfMirror = 0x141; // lane 7 - i of the half row
+constexpr int kDppRowBcast15 = 0x142;    // lane 15 of the row before
+constexpr int kDppRowBcast31 = 0x143;    // lane 31, into rows 2 and 3
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T x)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t u = (uint64_t)x;
+        return (T)(((uint64_t)dpp32<CTRL>((uint32_t)(u >> 32)) << 32) | dpp32<CTRL>((uint32_t)u));
+    } else {
+        return (T)dpp32<CTRL>((uint32_t)x);
+    }
+}
+
+// The value of x in lane `lane` (uniform), for every lane.
+template <typename T>
+__device__ __forceinline__ T lane_value(T x, int lane)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t u = (uint64_t)x;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+        return (T)(((uint64_t)hi << 32) | lo);
+    } else {
+        return (T)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes of a full wave: a scan inside each
+// row by shifts of 1, 2, 4 and 8 lanes, then each row adds the totals of the
+// rows before it.
 __device__ __forceinline__ int wave_inclusive_scan(int x)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int y = __shfl_up(x, d, kWave);
-        if (lane_id() >= d)
-            x += y;
-    }
-    return x;
+    uint32_t v = (uint32_t)x;
+    v += dpp32<kDppRowShr1>(v);
+    v += dpp32<kDppRowShr2>(v);
+    v += dpp32<kDppRowShr4>(v);
+    v += dpp32<kDppRowShr8>(v);
+    v += dpp32<kDppRowBcast15, 0xA>(v);
+    v += dpp32<kDppRowBcast31, 0xC>(v);
+    return (int)v;
+}
+
+// Reduction of a full wave by a commutative, associative op: inside each row
+// (quads, then mirrored half rows, then mirrored rows), then over the four
+// rows' results in scalar registers; every lane gets the result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op)
+{
+    x = op(x, dpp_move<kDppQuadXor1>(x));
+    x = op(x, dpp_move<kDppQuadXor2>(x));
+    x = op(x, dpp_move<kDppRowHalfMirror>(x));
+    x = op(x, dpp_move<kDppRowMirror>(x));
+    return op(op(lane_value(x, 0), lane_value(x, 16)), op(lane_value(x, 32), lane_value(x, 48)));
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x)
 {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        x += __shfl_xor(x, d, kWave);
-    return x;
+    return wave_reduce(x, [](T a, T b) { return a + b; });
 }
 
 // Ascending bitonic sort of s[0..n) in LDS, n a power of two.  Ends with a
@@ -72,23 +135,13 @@ __device__ void bitonic_sort(K *s, int n)
 template <typename T>
 __device__ __forceinline__ T wave_min(T x)
 {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) {
-        T y = __shfl_xor(x, d, kWave);
-        x = y < x ? y : x;
-    }
-    return x;
+    return wave_reduce(x, [](T a, T b) { return b < a ? b : a; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T x)
 {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) {
-        T y = __shfl_xor(x, d, kWave);
-        x = y > x ? y : x;
-    }
-    return x;
+    return wave_reduce(x, [](T a, T b) { return b > a ? b : a; });
 }
 
 // ---------------------------------------------------------------------------
@@ -128,7 +181,9 @@ __device__ __forceinline__ void wave_sort_run(K (&v)[E])
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int idx = e * kWave + lane;
-                    const K o = __shfl_xor(v[e], j, kWave);
+                    const K o = j == 1   ? dpp_move<kDppQuadXor1>(v[e])
+                                : j == 2 ? dpp_move<kDppQuadXor2>(v[e])
+                                         : __shfl_xor(v[e], j, kWave);
                     const bool keep_min = ((idx & j) == 0) == ((idx & k) == 0);
                     v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
                 }

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(NT) void dedup_kernel(int32_t q, int32_t k, int32_t
         int base = 0;
         if (lane_id() == 0 && b)
             base = atomicAdd(&sCount, __popcll(b));
-        base = __shfl(base, 0, kWave);
+        base = lane_value(base, 0);
         if (own)
             list[base + ballot_rank(b)] = key[e];
     }

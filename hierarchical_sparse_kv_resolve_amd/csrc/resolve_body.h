@@ -109,8 +109,20 @@ __device__ __forceinline__ void rank_sort_small(K *s, int n)
     }
     for (; j < j1; ++j)
         below += s[j] < mine ? 1 : 0;
-    for (int d = 1; d < P; d <<= 1)
-        below += __shfl_xor(below, d, kWave);
+    // the P lanes of one key add their counts: inside rows by DPP, across
+    // rows by shuffles (P is uniform)
+    if (P >= 2)
+        below += dpp_move<kDppQuadXor1>(below);
+    if (P >= 4)
+        below += dpp_move<kDppQuadXor2>(below);
+    if (P >= 8)
+        below += dpp_move<kDppRowHalfMirror>(below);
+    if (P >= 16)
+        below += dpp_move<kDppRowMirror>(below);
+    if (P >= 32)
+        below += __shfl_xor(below, 16, kWave);
+    if (P >= 64)
+        below += __shfl_xor(below, 32, kWave);
     __syncthreads();
     if (el < n && part == 0)
         s[below] = mine;
@@ -417,7 +429,7 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
         int wbase = 0;
         if (lane_id() == 0 && mb)
             wbase = atomicAdd(&sMiss, __popcll(mb));
-        wbase = __shfl(wbase, 0, kWave);
+        wbase = lane_value(wbase, 0);
         if (miss) {
             const int32_t row = hkey[h];
             if (a.bw > 0)
@@ -585,8 +597,8 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
                     }
                     const uint64_t found = __ballot(pick >= 0);
                     const int src = found ? __ffsll((unsigned long long)found) - 1 : 0;
-                    pick = __shfl(pick, src, kWave);
-                    pick_below = __shfl(pick_below, src, kWave);
+                    pick = lane_value(pick, src);
+                    pick_below = lane_value(pick_below, src);
                     if (lane_id() == 0) {
                         sPick[0] = pick < 0 ? 0 : pick;
                         sPick[1] = pick_below;
@@ -638,7 +650,7 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
                 sum += c[q];
             }
             const int incl = wave_inclusive_scan(sum);
-            const int half = __shfl(incl, kWave / 2 - 1, kWave);
+            const int half = lane_value(incl, kWave / 2 - 1);
             int run = incl - sum - (lane_id() >= kWave / 2 ? half : 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
