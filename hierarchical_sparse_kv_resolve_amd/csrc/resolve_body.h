@@ -165,24 +165,65 @@ __device__ __forceinline__ void hfind_many(const int32_t *hkey, int hs, const in
     }
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Chunks of the decoded rows a block appends: per layer, the host copy, then
+// (unless the tail write is deferred) the tail copy, of R/16 chunks each.
+__device__ __forceinline__ int append_per_layer(const ResolveArgs &a)
+{
+    return (a.sh.R / 16) * (a.sh.T > 0 && !a.defer_tail ? 2 : 1);
+}
+
+// A thread's first chunk to append (chunk threadIdx.x) and the store it goes
+// to, loaded before the request's length is known: the chunk does not depend
+// on it, so the append waits for one memory round trip instead of two.
+struct AppendChunk {
+    u32x4 v;
+    uint8_t *base;  // the layer's host store or tail
+};
+
+__device__ __forceinline__ AppendChunk append_first(const ResolveArgs &a, int i)
+{
+    AppendChunk f;
+    f.v = u32x4{0u, 0u, 0u, 0u};
+    f.base = nullptr;
+    const int per_layer = append_per_layer(a);
+    const int c = threadIdx.x;
+    if (a.new_rows && c < per_layer * a.sh.n_layers) {
+        const int C = a.sh.R / 16;
+        const int l = c / per_layer;
+        const int e = c - l * per_layer;
+        f.v = *reinterpret_cast<const u32x4 *>(a.new_rows + ((int64_t)l * a.n + i) * a.sh.R +
+                                               (e % C) * 16);
+        f.base = e < C ? a.layers[l].host : a.layers[l].tail;
+    }
+    return f;
+}
+
 // The request's decoded row of every layer into tail slot L mod T and, written
 // through, host row L (what kvr_append_rows does), by all threads of the block.
-// A deferred append writes the host row only.
-__device__ __forceinline__ void append_row(const ResolveArgs &a, int i, int r, int32_t L)
+// A deferred append writes the host row only.  `first` is append_first's.
+__device__ __forceinline__ void append_row(const ResolveArgs &a, int i, int r, int32_t L,
+                                           const AppendChunk &first)
 {
     const Shape &sh = a.sh;
     const int C = sh.R / 16;
-    const int per_layer = C * (sh.T > 0 && !a.defer_tail ? 2 : 1);
+    const int per_layer = append_per_layer(a);
     for (int c = threadIdx.x; c < per_layer * sh.n_layers; c += NT) {
         const int l = c / per_layer;
         const int e = c - l * per_layer;
         const int off = (e % C) * 16;
-        const LayerPtrs lp = a.layers[l];
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(
-            a.new_rows + ((int64_t)l * a.n + i) * sh.R + off);
-        uint8_t *dst = (e < C) ? lp.host + ((int64_t)r * sh.host_rows + L) * sh.R + off
-                               : lp.tail + ((int64_t)r * sh.T + L % sh.T) * sh.R + off;
+        u32x4 v;
+        uint8_t *base;
+        if (c == (int)threadIdx.x) {
+            v = first.v;
+            base = first.base;
+        } else {
+            v = *reinterpret_cast<const u32x4 *>(a.new_rows + ((int64_t)l * a.n + i) * sh.R + off);
+            base = e < C ? a.layers[l].host : a.layers[l].tail;
+        }
+        uint8_t *dst = (e < C) ? base + ((int64_t)r * sh.host_rows + L) * sh.R + off
+                               : base + ((int64_t)r * sh.T + L % sh.T) * sh.R + off;
         *reinterpret_cast<u32x4 *>(dst) = v;
     }
 }
@@ -229,7 +270,35 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
     const int r = a.req_ids ? a.req_ids[i] : i;
     int k = a.sel_count ? a.sel_count[i] : a.stride;
     const bool r_ok = r >= 0 && r < sh.n_req;
+    const bool call_ok = r_ok && k >= 0 && k <= a.stride;
+    const int32_t *sel = a.sel + (int64_t)i * a.stride;
+    uint32_t *loc = a.loc + (int64_t)i * a.stride;
+    int32_t *tag = a.tag + (int64_t)r * sh.B;
+    uint32_t *stamp = a.stamp + (int64_t)r * sh.B;
+
+    // Every load that needs only the call's arguments is issued before any
+    // is used, so their round trips overlap: the request's length, this
+    // thread's first chunk to append, its selection rows (the head of the
+    // longest dependent chain: row -> page map), and the tags and stamps of
+    // its slots (b = e*NT + tid).
     int32_t L = r_ok ? a.L[r] : 0;
+    const AppendChunk first = append_first(a, i);
+    int32_t p_in[EK];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        const int j = e * NT + tid;
+        p_in[e] = call_ok && j < k ? sel[j] : 0;
+    }
+    int32_t t[EB];
+    uint32_t st[EB];
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+        const int b = e * NT + tid;
+        t[e] = call_ok && b < sh.B ? tag[b] : -1;
+        st[e] = call_ok && b < sh.B ? stamp[b] : 0u;
+    }
+    const uint32_t clk = call_ok ? a.clock[r] : 0u;
+
     // Append first when asked (it fails alone, as the separate call would):
     // every thread has read L before thread 0 publishes L + 1 after a barrier.
     bool appended = false;
@@ -239,7 +308,7 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
             if (L < 0 || (int64_t)L >= sh.host_rows) {
                 code = KVR_E_CAPACITY;
             } else {
-                append_row(a, i, r, L);
+                append_row(a, i, r, L, first);
                 appended = true;
                 code = KVR_OK;
                 ++L;
@@ -250,7 +319,7 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
         if (tid == 0 && a.append_pos)
             a.append_pos[i] = appended ? L - 1 : -1;
     }
-    if (!r_ok || k < 0 || k > a.stride) {
+    if (!call_ok) {
         if (appended) {
             __syncthreads();
             if (tid == 0)
@@ -259,28 +328,6 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
         fail_request(a, i, k < 0 ? 0 : (k > a.stride ? a.stride : k), KVR_E_ARG);
         return;
     }
-    const int32_t *sel = a.sel + (int64_t)i * a.stride;
-    uint32_t *loc = a.loc + (int64_t)i * a.stride;
-    int32_t *tag = a.tag + (int64_t)r * sh.B;
-    uint32_t *stamp = a.stamp + (int64_t)r * sh.B;
-
-    // The selection rows (head of the longest dependent chain: row -> page
-    // map), then the tags and stamps of this thread's slots (b = e*NT + tid).
-    int32_t p_in[EK];
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        const int j = e * NT + tid;
-        p_in[e] = j < k ? sel[j] : 0;
-    }
-    int32_t t[EB];
-    uint32_t st[EB];
-#pragma unroll
-    for (int e = 0; e < EB; ++e) {
-        const int b = e * NT + tid;
-        t[e] = b < sh.B ? tag[b] : -1;
-        st[e] = b < sh.B ? stamp[b] : 0u;
-    }
-    const uint32_t clk = a.clock[r];
     const int32_t tail_lo = sh.T > 0 ? max(L - sh.T, 0) : L;
     const int32_t *pmap = a.page_map + (int64_t)r * sh.n_pages;
     const uint8_t *hvalid = a.host_valid + (int64_t)r * sh.n_pages;
@@ -463,8 +510,9 @@ __device__ __forceinline__ void resolve_body(const ResolveArgs &a, int i, uint8_
                 sRedU[wave_id()] = (uint32_t)incl;
             __syncthreads();
             int base = 0;
-            for (int w = 0; w < wave_id(); ++w)
-                base += (int)sRedU[w];
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                base += w < wave_id() ? (int)sRedU[w] : 0;
             sChunk[tid] = base + incl - cnt;
             __syncthreads();
 #pragma unroll
