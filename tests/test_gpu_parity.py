@@ -490,6 +490,19 @@ def test_gather_resolve_entry_point_equals_separate_calls():
             g.close()
 
 
+@pytest.mark.parametrize("k,B", [(512, 512), (513, 512), (512, 513), (1, 1), (37, 512)])
+def test_small_call_parity(k, B):
+    """Small calls: one selected row and one hot slot, a few rows against a
+    large budget, and selections and budgets around 512, on the one-stream
+    and merged schedules."""
+    ready = min(0.97, max(0.7, 1.0 - 0.7 * B / k))
+    cfg = tiny(2).with_(name=f"small{k}x{B}", n_req=3, H=6000, T=64, k=k, B=B,
+                        payload_layers=2, R=48, steps=4, sel="uniform", ready_frac=ready)
+    print(f"[parity] small call k={k} B={B}", flush=True)
+    for sched in (dict(), dict(fused=True, merged=True)):
+        _run_parity(cfg, **sched)
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
 @pytest.mark.parametrize("ek", [1, 2, 4, 8])
 def test_every_resolve_instance(ek, eb):
