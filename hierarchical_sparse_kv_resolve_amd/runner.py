@@ -17,9 +17,14 @@ stream-ordered calls with no host synchronisation.  The one-stream schedule:
                        reuse_locations(SHARED_SOURCE) for each Reuse layer
                        (an alias: no bytes move)
 
-The prefetch and fused schedules (GpuRun.step) reorder the fills and gathers
-of the same calls; the fused one fills from host and gathers in one launch
-(fused_gather_rows).
+The other schedules (GpuRun.step) reorder the fills and gathers of the same
+calls: prefetch issues the host fills of layer groups on a side stream ahead
+of their gathers; fused fills from host and gathers in one launch
+(fused_gather_rows); pipelined runs each resolve on the current stream while
+the previous fused launch gathers on a side stream; merged (the default of
+bench.py) issues each resolve in one launch with the gather of the resolve
+before it (gather_resolve_rows) and leaves the last gather to finish().
+Every schedule gives the same results.
 
 `inputs` supplies shapes and seeded contents (cfg, page_map, host_valid,
 fill_tail/fill_pool/fill_host, new_rows, selections).
