@@ -563,6 +563,36 @@ def test_random_shapes_parity(seed):
         _run_parity(cfg, **sched)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_back_to_back(seed):
+    """Seeded random shapes (every workload kind, verify blocks of 2 to 4
+    queries, selections up to 1500 rows, tight to roomy budgets, 16- to
+    1152-byte rows, 1 to 4 layers or resolving groups, 2 to 6 steps) issued
+    back to back on the merged and pipelined schedules, so every launch but
+    the first gathers the previous selection beside the next resolve;
+    outputs of the last step and the final state equal the oracle's."""
+    rng = np.random.default_rng(7000 + seed)
+    base = tiny([1, 2, 3, 4, 5][seed % 5])
+    big = seed % 4 == 0
+    H = int(rng.integers(300, 6000 if big else 3000))
+    k = int(rng.integers(1, min(1500 if big else 300, H // 3)))
+    kw = dict(name=f"b2b{seed}", n_req=int(rng.integers(1, 5)), H=H,
+              P=int(rng.choice([1, 7, 16, 64])), T=int(rng.choice([0, 3, 40, 129])), k=k,
+              B=int(rng.integers(max(1, k // 4), 2 * k + 40)),
+              R=int(rng.choice([16, 48, 656, 1152])), steps=int(rng.integers(2, 7)),
+              ready_frac=float(rng.choice([0.0, 0.3, 1.0])), seed=9000 + seed)
+    if base.q > 1:
+        kw["q"] = int(rng.integers(2, 5))
+    if base.reuse == "distinct":
+        kw["payload_layers"] = int(rng.integers(1, 5))
+    else:
+        kw["groups"] = int(rng.integers(1, 4))
+    cfg = base.with_(**kw)
+    print(f"[parity] back-to-back random shape {cfg}", flush=True)
+    for sched in (dict(merged=True), dict(pipelined=True)):
+        _back_to_back(cfg, sched)
+
+
 @pytest.mark.parametrize("c,kw", [(2, dict(k=600)), (2, dict(k=200)), (4, dict(k=300, q=2))])
 def test_long_history_parity(c, kw):
     """Histories of 1.3 M rows (16-byte rows keep the stores small): too long
