@@ -510,7 +510,9 @@ def test_every_resolve_instance(ek, eb):
     slots per thread of its 1024-thread workgroup: 1, 2, 4 or 8 each), in
     the resolve kernel and in the step kernel: a selection capacity just
     under ek * 1024 and a budget just under eb * 1024, on the one-stream,
-    fused and merged schedules."""
+    fused and merged schedules step by step (each resolve in a launch of its
+    own), then merged back to back (each resolve beside the previous
+    gather, in the step kernel's instance)."""
     k, B = ek * 1024 - 37, eb * 1024 - 5
     # enough ready pages that the pending rows mostly fit the budget, so the
     # victim selection runs (a few calls may still fail with E_CAPACITY)
@@ -520,6 +522,7 @@ def test_every_resolve_instance(ek, eb):
     print(f"[parity] instance {ek}x{eb}: k={k} B={B}", flush=True)
     for sched in (dict(), dict(fused=True), dict(fused=True, merged=True)):
         _run_parity(cfg, **sched)
+    _back_to_back(cfg, dict(merged=True))
 
 
 @pytest.mark.parametrize("c,B", [(2, 80), (2, 512), (3, 160), (3, 1024), (5, 120), (5, 2048)])
