@@ -1546,3 +1546,67 @@ def test_snapshot_resume_equals_continuous_run(c, kw):
     finally:
         a.close()
         b.close()
+
+
+def test_golden_trace_on_gpu():
+    """The stored 24-call LRU trace (tests/golden/lru_trace_small.json: its own
+    shape, page map, host-copy map and selections, with the expected results
+    written from the oracle by tests/golden/make_golden.py) replayed through
+    kvr_append_rows and kvr_resolve_rows: every call's status, locations and
+    fills, and the tags, stamps, clock and length after it, equal the stored
+    values.  This pins the HIP path to stored expectations that depend on
+    neither the input generator nor a live oracle run."""
+    import json
+    import os
+
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    path = os.path.join(os.path.dirname(__file__), "golden", "lru_trace_small.json")
+    fx = json.load(open(path))
+    H, P, T, B, R, M = fx["H"], fx["P"], fx["T"], fx["B"], fx["R"], fx["max_new"]
+    cap = max(len(c["sel"]) for c in fx["calls"])
+    pool_pages = max(fx["page_map"]) + 1
+    dev = "cuda"
+    i32 = torch.int32
+    ctx = kvr.Context(n_req=1, n_layers=1, history_rows=H, max_new_rows=M, page_rows=P,
+                      tail_rows=T, hot_slots=B, row_bytes=R, sel_cap=cap, pool_pages=pool_pages)
+    host = kvr.host_alloc((H + M) * R)
+    try:
+        L = torch.empty(1, dtype=i32, device=dev)
+        page_map = torch.tensor([fx["page_map"]], dtype=i32, device=dev)
+        host_valid = torch.tensor([fx["host_valid"]], dtype=torch.uint8, device=dev)
+        tag = torch.empty((1, B), dtype=i32, device=dev)
+        stamp = torch.empty((1, B), dtype=i32, device=dev)
+        clock = torch.empty(1, dtype=i32, device=dev)
+        ctx.bind_metadata(L, page_map, host_valid, tag, stamp, clock)
+        tail = torch.zeros((1, T, R), dtype=torch.uint8, device=dev)
+        pool = torch.zeros((pool_pages, P, R), dtype=torch.uint8, device=dev)
+        hot = torch.zeros((1, B, R), dtype=torch.uint8, device=dev)
+        ctx.bind_layer(0, tail, pool, hot, host)
+        ctx.init_state()
+        row = torch.zeros((1, 1, R), dtype=torch.uint8, device=dev)
+        app_status = torch.zeros(1, dtype=i32, device=dev)
+        loc = torch.empty((1, cap), dtype=i32, device=dev)
+        fills = torch.empty((1, B, 2), dtype=i32, device=dev)
+        fc = torch.empty(1, dtype=i32, device=dev)
+        status = torch.empty(1, dtype=i32, device=dev)
+        for c, (call, want) in enumerate(zip(fx["calls"], fx["expected"])):
+            if call["append"]:
+                ctx.append_rows(1, None, row, app_status)
+            k = len(call["sel"])
+            sel = torch.tensor([call["sel"]], dtype=i32, device=dev)
+            ctx.resolve_rows(1, None, sel, None, k, loc, fills, fc, 0, status)
+            torch.cuda.synchronize()
+            assert int(status[0]) == want["status"], c
+            got_loc = [int(x) & 0xFFFFFFFF for x in loc[0, :k].tolist()]
+            assert got_loc == want["loc"], c
+            n_f = int(fc[0])
+            assert fills[0, :n_f].tolist() == want["fills"], c
+            assert tag[0].tolist() == want["tag"], c
+            assert [int(x) & 0xFFFFFFFF for x in stamp[0].tolist()] == want["stamp"], c
+            assert int(clock[0]) & 0xFFFFFFFF == want["clock"], c
+            assert int(L[0]) == want["L"], c
+    finally:
+        torch.cuda.synchronize()
+        ctx.close()
+        kvr.host_free(host)
