@@ -3,6 +3,8 @@ for the workload, schedule and gather source it was measured on; launch
 records group by kernel; layer groups split the payload layers."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -60,3 +62,15 @@ def test_cpu_baseline_on_a_request_sample():
     assert "requests 0..1 of 4" in out["sample"] and out["cores"] <= 2
     full = bench.cpu_baseline(cfg, 2, budget_s=2.0, min_s=0.05)
     assert f"all {cfg.n_req} requests" in full["sample"]
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits at once with a message
+    (before any GPU work)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
