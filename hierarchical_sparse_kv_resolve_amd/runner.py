@@ -261,8 +261,10 @@ class GpuRun:
             else:
                 src, count, stride = sel, None, k
             loc, fills, fc = self.loc[g], self.fills[g], self.fill_count[g]
-            pipelined = bool(prefetch_groups) or fused
-            fill_layer = -1 if pipelined else 0
+            # the host fills are issued apart from the resolve (prefetch
+            # groups, or the fused fill-and-gather), not by the resolve call
+            fills_apart = bool(prefetch_groups) or fused
+            fill_layer = -1 if fills_apart else 0
             if self.fuse_append and g == 0:
                 ctx.append_resolve_rows(n, None, self.rows_dev[s], self.append_status, src, count,
                                         stride, loc, fills, fc, fill_layer, self.status[g],
@@ -323,7 +325,7 @@ class GpuRun:
                 if g == cfg.groups - 1 or serialize:
                     main.wait_event(filled)
                     main.wait_event(resident)
-            elif cfg.reuse != "distinct" and pipelined:
+            elif cfg.reuse != "distinct" and fills_apart:
                 # One physical source: this layer's fill and gather run on the
                 # side stream while the main stream resolves the next layer
                 # (resolve touches metadata only).  The side stream keeps the
@@ -353,7 +355,7 @@ class GpuRun:
                 for _ in range(1, cfg.layers_per_group):
                     ctx.reuse_locations(kvr.REUSE_SHARED_SOURCE, None, n, None, loc, None, count,
                                         stride, stream=main)
-            elif not pipelined:
+            elif not fills_apart:
                 layers = list(range(1 if fill_layer == 0 else 0, self.nl))
                 if layers:
                     ctx.reuse_locations(kvr.REUSE_DISTINCT_PAYLOAD, layers, n, None, loc,
