@@ -1610,3 +1610,44 @@ def test_golden_trace_on_gpu():
         torch.cuda.synchronize()
         ctx.close()
         kvr.host_free(host)
+
+
+def test_reuse_locations_copies_the_vector():
+    """kvr_reuse_locations with a destination vector: the shared-source mode
+    copies the location words (and moves no payload); the distinct-payload
+    mode copies them and replays the call's fills into the listed layers
+    (again, here: the hot payload stays the oracle's).  Ragged counts: each
+    request's first count[i] words are copied, the rest of its row of the
+    destination is left as it was."""
+    import torch
+    from hierarchical_sparse_kv_resolve_amd import kvr
+    cfg = tiny(2).with_(name="reuse_copy", payload_layers=3, steps=1)
+    inputs = Inputs(cfg, max_new=cfg.steps)
+    gpu = _gpu_run(inputs)
+    run = OracleRun(inputs)
+    try:
+        gpu.stage([0])
+        gpu.step(0)
+        o = run.step(0)
+        n, cap = cfg.n_req, cfg.sel_cap
+        loc = gpu.loc[0]
+        counts = torch.tensor([cap, cap // 2, 0][:n] + [cap] * max(0, n - 3), dtype=torch.int32,
+                              device="cuda")
+        for mode, layers in ((kvr.REUSE_SHARED_SOURCE, None),
+                             (kvr.REUSE_DISTINCT_PAYLOAD, [1, 2])):
+            dst = torch.full((n, cap), -7, dtype=torch.int32, device="cuda")
+            status = torch.zeros(n, dtype=torch.int32, device="cuda")
+            gpu.ctx.reuse_locations(mode, layers, n, None, loc, dst, counts, cap,
+                                    gpu.fills[0], gpu.fill_count[0], status)
+            torch.cuda.synchronize()
+            got, want = dst.cpu().numpy(), loc.cpu().numpy()
+            for i, c in enumerate(counts.cpu().tolist()):
+                assert np.array_equal(got[i, :c], want[i, :c]), (mode, i)
+                assert (got[i, c:] == -7).all(), (mode, i)
+            assert (status.cpu().numpy() == 0).all()
+        assert np.array_equal(loc.cpu().numpy().view(np.uint32),
+                              o["groups"][0]["loc"].astype(np.uint32))
+        for l in range(cfg.payload_layers):
+            assert np.array_equal(gpu.hot[l].cpu().numpy(), run.src.hot[l])
+    finally:
+        gpu.close()
